@@ -1,0 +1,230 @@
+"""Python binding of libkda (KDA gated delta-rule recurrence on MI355X / gfx950).
+
+Argument marshalling only: every step of the recurrence runs in the HIP kernels
+of ``libkda.so``; this module turns torch tensors / numpy arrays into pointers,
+sizes and the current HIP stream, calls the C ABI declared in ``include/kda.h``
+under the same names, and raises ``KdaError`` on a non-zero status.  There is no
+CPU fallback: importing fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE = 0, 1, 2, 3
+KDA_ERR_PAGE_RANGE, KDA_ERR_PAGE_ALIAS, KDA_ERR_CKPT_ALIGN, KDA_ERR_CKPT_RANGE = 4, 5, 6, 7
+KDA_ERR_SEQ, KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_POOL = 8, 9, 10, 11
+STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+                4: "KDA_ERR_PAGE_RANGE", 5: "KDA_ERR_PAGE_ALIAS", 6: "KDA_ERR_CKPT_ALIGN",
+                7: "KDA_ERR_CKPT_RANGE", 8: "KDA_ERR_SEQ", 9: "KDA_ERR_WORKSPACE",
+                10: "KDA_ERR_HIP", 11: "KDA_ERR_POOL"}
+KDA_F32, KDA_BF16 = 0, 1
+HASH_BLOCK = 512
+CHUNK = 64
+
+EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset",
+           "kda_prefill_workspace_bytes", "kda_prefill_chunked", "kda_decode_step",
+           "kda_checkpoint_write", "kda_checkpoint_restore", "kda_profile_enable",
+           "kda_profile_read")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class kda_pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("page_bytes", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+class kda_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libkda.so is not built ({LIB_PATH}); run "
+                      "`python -m hybrid_prefix_cache_amd.build` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_PP = ctypes.POINTER(kda_pool)
+_sig = {
+    "kda_version": (_i32, []),
+    "kda_last_error": (ctypes.c_char_p, []),
+    "kda_pool_check": (ctypes.c_int, [_PP]),
+    "kda_state_offset": (_i64, [_PP, _i32, _i32]),
+    "kda_prefill_workspace_bytes": (_sz, [_PP, _i64, _i32, _i32, ctypes.c_int]),
+    "kda_prefill_chunked": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
+                                           _i32, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, _P, _sz,
+                                           _P]),
+    "kda_decode_step": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
+                                       _i32, _P, _P, _P]),
+    "kda_checkpoint_write": (ctypes.c_int, [_PP, _P, _P, _i32, _P]),
+    "kda_checkpoint_restore": (ctypes.c_int, [_PP, _P, _P, _i32, _P]),
+    "kda_profile_enable": (ctypes.c_int, [_i32]),
+    "kda_profile_read": (_i32, [ctypes.POINTER(kda_kernel_stat), _i32, _i32]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _dptr(x):
+    """Device pointer of a CUDA/HIP torch tensor (must be contiguous), an int,
+    or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("device tensors must be contiguous")
+    return x.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+class _HostArr:
+    """Keeps a contiguous numpy copy alive while its pointer is in use."""
+
+    def __init__(self, x, dtype):
+        self.a = None if x is None else np.ascontiguousarray(np.asarray(x), dtype=dtype)
+
+    @property
+    def ptr(self):
+        return None if self.a is None else self.a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int):
+    if status != KDA_OK:
+        raise KdaError(status, kda_last_error())
+
+
+def make_pool(base, page_bytes: int, num_pages: int, num_heads: int, d_k: int, d_v: int | None = None):
+    """Pool descriptor over caller-owned device memory (a torch tensor or a raw
+    device pointer)."""
+    return kda_pool(_dptr(base), int(page_bytes), int(num_pages), int(num_heads), int(d_k),
+                    int(d_k if d_v is None else d_v))
+
+
+# ---------------------------------------------------------------------------
+# the C ABI under the same names
+# ---------------------------------------------------------------------------
+def kda_version() -> int:
+    return int(_lib.kda_version())
+
+
+def kda_last_error() -> str:
+    return _lib.kda_last_error().decode()
+
+
+def kda_pool_check(pool: kda_pool) -> int:
+    return int(_lib.kda_pool_check(ctypes.byref(pool)))
+
+
+def kda_state_offset(pool: kda_pool, page: int, head: int) -> int:
+    return int(_lib.kda_state_offset(ctypes.byref(pool), page, head))
+
+
+def kda_prefill_workspace_bytes(pool: kda_pool, total_tokens: int, num_seqs: int, num_ckpts: int,
+                                in_dtype: int) -> int:
+    return int(_lib.kda_prefill_workspace_bytes(ctypes.byref(pool), total_tokens, num_seqs,
+                                                num_ckpts, in_dtype))
+
+
+def kda_prefill_chunked(pool, q, k, v, g, beta, o, cu_seqlens, *, start_pos=None,
+                        state_in_page=None, state_out_page=None, ckpt_cu=None, ckpt_pos=None,
+                        ckpt_page=None, workspace=None, workspace_bytes=None, chunk_size=CHUNK,
+                        hash_block=HASH_BLOCK, in_dtype=None, out_dtype=None, stream=None):
+    """q, k, g: [T, H, d_k]; v, o: [T, H, d_v]; beta: [T, H] (device tensors).
+    Host metadata as sequences / numpy arrays (see include/kda.h).  The
+    workspace is a device tensor (uint8) of at least kda_prefill_workspace_bytes."""
+    cu = _HostArr(cu_seqlens, np.int64)
+    ns = len(cu.a) - 1
+    sp = _HostArr(start_pos, np.int64)
+    si = _HostArr(state_in_page, np.int32)
+    so = _HostArr(state_out_page, np.int32)
+    ccu = _HostArr(ckpt_cu, np.int32)
+    cpos = _HostArr(ckpt_pos, np.int64)
+    cpg = _HostArr(ckpt_page, np.int32)
+    ind = _dtype_code(q) if in_dtype is None else in_dtype
+    outd = _dtype_code(o) if out_dtype is None else out_dtype
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0)
+    st = _lib.kda_prefill_chunked(ctypes.byref(pool), _dptr(q), _dptr(k), _dptr(v), _dptr(g),
+                                  _dptr(beta), ind, _dptr(o), outd, ns, cu.ptr, sp.ptr, si.ptr,
+                                  so.ptr, ccu.ptr, cpos.ptr, cpg.ptr, chunk_size, hash_block,
+                                  _dptr(workspace), workspace_bytes, _stream(stream))
+    _check(st)
+
+
+def kda_decode_step(pool, q, k, v, g, beta, o, page_in, page_out, *, n=None, in_dtype=None,
+                    out_dtype=None, stream=None):
+    """q, k, g: [n, H, d_k]; v, o: [n, H, d_v]; beta: [n, H]; page_in/page_out:
+    int32 device tensors [n]."""
+    n = int(page_in.numel()) if n is None else n
+    ind = _dtype_code(q) if in_dtype is None else in_dtype
+    outd = _dtype_code(o) if out_dtype is None else out_dtype
+    st = _lib.kda_decode_step(ctypes.byref(pool), _dptr(q), _dptr(k), _dptr(v), _dptr(g),
+                              _dptr(beta), ind, _dptr(o), outd, n, _dptr(page_in),
+                              _dptr(page_out), _stream(stream))
+    _check(st)
+
+
+def kda_checkpoint_write(pool, src_active, dst_ckpt, *, stream=None):
+    s, d = _HostArr(src_active, np.int32), _HostArr(dst_ckpt, np.int32)
+    _check(_lib.kda_checkpoint_write(ctypes.byref(pool), s.ptr, d.ptr, len(s.a), _stream(stream)))
+
+
+def kda_checkpoint_restore(pool, src_ckpt, dst_active, *, stream=None):
+    s, d = _HostArr(src_ckpt, np.int32), _HostArr(dst_active, np.int32)
+    _check(_lib.kda_checkpoint_restore(ctypes.byref(pool), s.ptr, d.ptr, len(s.a), _stream(stream)))
+
+
+def kda_profile_enable(on: bool = True):
+    _check(_lib.kda_profile_enable(1 if on else 0))
+
+
+def kda_profile_read(reset: bool = True) -> dict:
+    """{kernel name: (launches, total_ms)} since the last reset (synchronises
+    the recorded events)."""
+    n = _lib.kda_profile_read(None, 0, 0)
+    arr = (kda_kernel_stat * max(1, n))()
+    got = _lib.kda_profile_read(arr, n, 1 if reset else 0)
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(got)}
+
+
+def raw_call(name: str, *args):
+    """Direct access to an exported symbol (for ABI tests)."""
+    return getattr(_lib, name)(*args)

@@ -1,0 +1,77 @@
+// kda_launch.h -- kernel-argument structs and launch entry points shared by the
+// host launcher (kda_api.cpp) and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_meta.h"
+
+namespace kda {
+
+struct PrepArgs {
+  const void* q;
+  const void* k;
+  const void* g;
+  const void* beta;
+  const SeqEntry* seqs;
+  int32_t num_seqs;
+  int32_t H;
+  uint8_t* inter;
+  int64_t blk_bytes;
+};
+
+struct ScanArgs {
+  const void* v;
+  void* o;
+  int32_t out_bf16;
+  int32_t H;
+  const SeqEntry* seqs;
+  const int32_t* order;  // sequences by descending length
+  const CkptEntry* ckpts;
+  int32_t npairs;  // num_seqs * H
+  int32_t pad;
+  const uint8_t* inter;
+  int64_t blk_bytes;
+  uint8_t* pool;
+  int64_t page_bytes;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  void* o;
+  const int32_t* page_in;
+  const int32_t* page_out;
+  uint8_t* pool;
+  int64_t page_bytes;
+  int32_t num_pages;
+  int32_t H;
+  int32_t out_bf16;
+  int32_t n;
+};
+
+constexpr int kCopyPairsPerLaunch = 448;
+constexpr int kPieceBytes = 64 * 1024;
+
+struct CopyArgs {
+  uint8_t* pool;
+  int64_t page_bytes;
+  int64_t state_bytes;  // bytes copied per page
+  int32_t pieces;       // ceil(state_bytes / kPieceBytes)
+  int32_t npairs;
+  int32_t src[kCopyPairsPerLaunch];
+  int32_t dst[kCopyPairsPerLaunch];
+};
+static_assert(sizeof(CopyArgs) <= 4096, "kernel argument budget");
+static_assert(sizeof(MetaFillArgs) <= 4096, "kernel argument budget");
+
+hipError_t launch_meta_fill(const MetaFillArgs& a, hipStream_t st);
+hipError_t launch_prep(int D, bool bf16, const PrepArgs& a, int total_chunks, hipStream_t st);
+hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st);
+hipError_t launch_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,219 @@
+/*
+ * kda.h -- C ABI of libkda: the KDA gated delta-rule recurrence on one
+ * MI355X (gfx950), with sparse state checkpoints over a paged state pool.
+ *
+ * Passages this interface implements (pages cited by title and section):
+ *
+ *  [ARCH]  "Kimi K3 -- Lesson 01 - Architecture map" (gentlecold.top),
+ *          section "两种 Attention，两种状态": per head a state S in
+ *          R^(d_k x d_v); each token decays S by a channel-wise forget gate
+ *          Diag(alpha_t), writes (k_t, v_t) by the delta rule with beta_t, and
+ *          reads o_t = S_t^T q_t; prefill is chunk-parallel with the state
+ *          carried from chunk to chunk, decode is a single-token update.
+ *  [AFF]   "KIMI K3 경량 복제에서 본 KDA의 AI 인프라 과제" (acpost.vercel.app),
+ *          sections 1.1/1.3 (per-token affine map S_t = M_t S_{t-1} + b_t; a
+ *          segment collapses to one affine map, associative, not commutative)
+ *          and 2.1 (decode reads a fixed-size state, not the history).
+ *  [CKPT]  "Cache de préfixe hybride KDA–MLA" (mkdocs.reaper.mx), sections
+ *          "La solution" (recurrent-state checkpoints only at a sparse subset
+ *          of 512-token hash-block ends), "Le fonctionnement du prefill"
+ *          (after a forward pass the kernel persists the state at the last
+ *          hash-aligned position it processed; checkpoints are read-only: a hit
+ *          copies one into the request's private state, new checkpoints go to
+ *          fresh slots) and "La recherche en deux étages" (hits are multiples
+ *          of the hash block).
+ *  [PAGE]  same page, section "La mise en page unifiée": states live in a pool
+ *          of pages of one fixed byte size; inside a page the states of all
+ *          heads are stored contiguously, head after head.
+ *
+ * Recurrence (decay first, then the delta-rule write, then the read):
+ *     S' = Diag(exp(g_t)) S_{t-1};  u = v_t - S'^T k_t;
+ *     S_t = S' + beta_t k_t u^T;    o_t = S_t^T q_t.
+ * The gate is passed as g = log(alpha).
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are HIP device memory owned by the caller; host pointers
+ *    are read before the call returns.  The library keeps no pointer past a
+ *    call and allocates no device memory.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is complete once that stream has synchronised.  Calls on one stream run
+ *    in call order, so a restore completes before a later prefill or decode on
+ *    the same stream reads the restored page.
+ *  - All arguments are validated before anything is enqueued; a non-KDA_OK
+ *    status means nothing was enqueued, except KDA_ERR_HIP (a launch failed
+ *    after validation; earlier launches of the same call may have run).
+ *  - kda_last_error() returns a thread-local description of the last failure.
+ *  - No exception or abort crosses this interface.
+ *  - Floating-point reductions use no atomics: repeated calls on the same
+ *    inputs give bitwise-identical results.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  KDA_ERR_SHAPE = 2,       /* unsupported head dims, counts, chunk or hash sizes  */
+  KDA_ERR_DTYPE = 3,       /* unknown dtype code                                  */
+  KDA_ERR_PAGE_RANGE = 4,  /* a page index is outside [0, num_pages)              */
+  KDA_ERR_PAGE_ALIAS = 5,  /* a destination page repeats or is also read          */
+  KDA_ERR_CKPT_ALIGN = 6,  /* checkpoint position not a multiple of hash_block    */
+  KDA_ERR_CKPT_RANGE = 7,  /* checkpoint outside (start, start+len] or unordered  */
+  KDA_ERR_SEQ = 8,         /* bad cu_seqlens / start_pos                          */
+  KDA_ERR_WORKSPACE = 9,   /* workspace NULL, misaligned or too small             */
+  KDA_ERR_HIP = 10,        /* a HIP launch or runtime call failed                 */
+  KDA_ERR_POOL = 11        /* invalid pool descriptor                             */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Paged state pool [PAGE].  `base` is device memory of num_pages * page_bytes
+ * bytes.  Page p, head h holds one fp32 state S[d_k][d_v], row-major (row =
+ * key channel), at byte offset
+ *     p * page_bytes + h * d_k * d_v * 4
+ * Bytes past num_heads * d_k * d_v * 4 in a page are padding that no entry
+ * point reads or writes.  Requirements (kda_pool_check): base and page_bytes
+ * multiples of 256, page_bytes >= num_heads * d_k * d_v * 4, num_pages >= 1,
+ * num_heads >= 1, d_k == d_v in {64, 128}.  The pool is owned by the caller.
+ */
+typedef struct {
+  void* base;
+  int64_t page_bytes;
+  int32_t num_pages;
+  int32_t num_heads;
+  int32_t d_k;
+  int32_t d_v;
+} kda_pool;
+
+/* Library version, (major << 16) | minor. */
+int32_t kda_version(void);
+
+/* Thread-local text of the last non-KDA_OK status on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Validates a pool descriptor (no device access).  [PAGE] */
+kda_status kda_pool_check(const kda_pool* pool);
+
+/* Byte offset of (page, head) inside the pool, or -1 if the descriptor is
+ * invalid or page/head is out of range.  [PAGE] */
+int64_t kda_state_offset(const kda_pool* pool, int32_t page, int32_t head);
+
+/*
+ * Device workspace bytes kda_prefill_chunked needs for a call with these
+ * sizes (total_tokens = cu_seqlens[num_seqs], num_ckpts = ckpt_cu[num_seqs]).
+ * Returns 0 for invalid arguments.  The workspace holds the call's metadata
+ * tables and the per-(chunk, head) intermediates of the chunk form; it must be
+ * 256-byte aligned and is free for reuse once the stream passes the call.
+ */
+size_t kda_prefill_workspace_bytes(const kda_pool* pool, int64_t total_tokens, int32_t num_seqs,
+                                   int32_t num_ckpts, kda_dtype in_dtype);
+
+/*
+ * Chunk-parallel prefill of a packed batch of sequences [ARCH][AFF], with the
+ * state carried between 64-token chunks and sparse checkpoint stores [CKPT].
+ *
+ * Device tensors (token-major, all with `in_dtype`):
+ *   q, k, g : [total_tokens, H, d_k]   (g = log alpha, one gate per key channel)
+ *   v       : [total_tokens, H, d_v]
+ *   beta    : [total_tokens, H]
+ *   o       : [total_tokens, H, d_v] written in `out_dtype`
+ * Host metadata (read before return):
+ *   cu_seqlens     [num_seqs+1]  int64, cu_seqlens[0] == 0, non-decreasing;
+ *                  sequence s owns rows [cu_seqlens[s], cu_seqlens[s+1]).
+ *   start_pos      [num_seqs]    int64 or NULL (all 0): absolute position of the
+ *                  sequence's first token; must be a multiple of chunk_size.  A
+ *                  resume at boundary B passes start_pos = B and the restored
+ *                  page as state_in_page.
+ *   state_in_page  [num_seqs]    int32 or NULL: page holding S before the first
+ *                  token; -1 (or NULL) = zero state.
+ *   state_out_page [num_seqs]    int32 or NULL: page receiving S after the last
+ *                  token; -1 (or NULL) = not stored.  May equal the same
+ *                  sequence's state_in_page (in-place update).
+ *   ckpt_cu        [num_seqs+1]  int32 CSR offsets into ckpt_pos/ckpt_page, or
+ *                  NULL for no checkpoints.
+ *   ckpt_pos       absolute positions P: multiple of hash_block, strictly
+ *                  increasing per sequence, start < P <= start+len.  The
+ *                  checkpoint at P is the state after P tokens.
+ *   ckpt_page      destination page of each checkpoint (a fresh page).
+ * chunk_size must be 64; hash_block a positive multiple of 64 (512 in the
+ * pages).  workspace must hold kda_prefill_workspace_bytes(...) bytes.
+ * Destination pages (state_out_page, ckpt_page) must be distinct and must not
+ * be any state_in_page, apart from the in-place case above (KDA_ERR_PAGE_ALIAS).
+ *
+ * Numerics: bf16 inputs run the chunk products on bf16 MFMA with fp32
+ * accumulation and an fp32 carried state; fp32 inputs run them in fp32.
+ * Domain: the chunk form factors the decay as exp(+G) and exp(-G) with G the
+ * within-chunk prefix sum of g; it needs |G| < 80 in every channel of every
+ * chunk (mean log alpha > -1.25 per token).
+ */
+kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                               kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
+                               const int64_t* start_pos, const int32_t* state_in_page,
+                               const int32_t* state_out_page, const int32_t* ckpt_cu,
+                               const int64_t* ckpt_pos, const int32_t* ckpt_page,
+                               int32_t chunk_size, int32_t hash_block, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step for n requests [ARCH][AFF 2.1]: for each request r and head
+ * h, read S from page_in[r], apply one token (q, k, v, g, beta of row r), write
+ * S to page_out[r] and o.  The state is read and written exactly once.
+ *   q, k, g : [n, H, d_k]; v : [n, H, d_v]; beta : [n, H]  (in_dtype, device)
+ *   o       : [n, H, d_v] (out_dtype, device)
+ *   page_in, page_out : [n] int32 DEVICE arrays (so a step needs no host sync).
+ * page_out[r] == page_in[r] updates in place.  The caller guarantees that the
+ * page_out entries are distinct and that no page_out[r] equals page_in[r'] for
+ * r' != r.  Device-side: a request whose page index is outside [0, num_pages)
+ * touches no state and gets NaN outputs.  With the environment variable
+ * KDA_VALIDATE=1 the page tables are copied to the host and checked first
+ * (this synchronises the stream).
+ */
+kda_status kda_decode_step(const kda_pool* pool, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                           kda_dtype out_dtype, int32_t n, const int32_t* page_in,
+                           const int32_t* page_out, void* stream);
+
+/*
+ * Checkpoint write [CKPT]: copy the state bytes (num_heads * d_k * d_v * 4) of
+ * page src_active[i] to page dst_ckpt[i], i < n.  Host index arrays.  Pages in
+ * range; destinations distinct and never a source of the same call.
+ */
+kda_status kda_checkpoint_write(const kda_pool* pool, const int32_t* src_active,
+                                const int32_t* dst_ckpt, int32_t n, void* stream);
+
+/*
+ * Checkpoint restore [CKPT]: copy checkpoint page src_ckpt[i] into the
+ * request's private active page dst_active[i] (copy-on-write: the checkpoint
+ * itself is never modified).  Same rules as kda_checkpoint_write.
+ */
+kda_status kda_checkpoint_restore(const kda_pool* pool, const int32_t* src_ckpt,
+                                  const int32_t* dst_active, int32_t n, void* stream);
+
+/*
+ * Optional per-kernel timing (tracing aid).  When enabled, every kernel the
+ * library launches is bracketed by a pair of HIP events on its own stream;
+ * kda_profile_read synchronises those events and returns, per kernel name, the
+ * launch count and the summed duration in milliseconds since the last reset.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} kda_kernel_stat;
+
+kda_status kda_profile_enable(int32_t on);
+int32_t kda_profile_read(kda_kernel_stat* out, int32_t max_entries, int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

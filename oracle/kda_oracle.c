@@ -70,6 +70,112 @@ static inline double ld(const void* p, int dtype, int64_t i) {
 
 int kda_oracle_mutant(void) { return KDA_ORACLE_MUTANT; }
 
+/* One (sequence, head) pair: the token loop.  Compiled twice (Haswell-class
+   AVX2/FMA and baseline x86-64) and picked at load time by the CPU, so the
+   library runs on any x86-64 host; the arithmetic is the same plain loops
+   either way (the wider clone may contract a*b+c into one FMA). */
+__attribute__((target_clones("arch=haswell", "default")))
+static void run_pair(int32_t H, int32_t dk, int32_t dv, int32_t in_dtype, int32_t gate_is_alpha,
+                     const void* q, const void* k, const void* v, const void* gate,
+                     const void* beta, const double* s0, double* o, double* s_final,
+                     const int64_t* ckpt_pos, double* ckpt_out, int32_t n_sel, int32_t s,
+                     int32_t hs, int32_t h, int64_t bos, int64_t len, int64_t st, int32_t m,
+                     int32_t m_end, double* S, double* u, double* a, double* kk, double* qq) {
+  const int64_t SD = (int64_t)dk * dv;
+  if (s0)
+    memcpy(S, s0 + ((int64_t)s * n_sel + hs) * SD, sizeof(double) * SD);
+  else
+    memset(S, 0, sizeof(double) * SD);
+
+  for (int64_t t = 0; t < len; ++t) {
+    const int64_t row = (bos + t) * H + h; /* (token, head) row index */
+    const double b = ld(beta, in_dtype, row);
+    for (int32_t c = 0; c < dk; ++c) {
+      const double gv = ld(gate, in_dtype, row * dk + c);
+      a[c] = gate_is_alpha ? gv : exp(gv);
+      kk[c] = ld(k, in_dtype, row * dk + c);
+      qq[c] = ld(q, in_dtype, row * dk + c);
+    }
+    for (int32_t j = 0; j < dv; ++j) u[j] = ld(v, in_dtype, row * dv + j);
+
+#if KDA_ORACLE_MUTANT == 2
+    /* mistake: read before this token's update */
+    if (o) {
+      double* orow = o + ((bos + t) * n_sel + hs) * dv;
+      for (int32_t j = 0; j < dv; ++j) orow[j] = 0.0;
+      for (int32_t c = 0; c < dk; ++c)
+        for (int32_t j = 0; j < dv; ++j) orow[j] += S[c * dv + j] * qq[c];
+    }
+#endif
+
+#if KDA_ORACLE_MUTANT == 5
+    /* mistake: literal bracket reading, decay only inside the erase term:
+       S <- S - beta k (k^T Diag(a) S) + beta k v^T */
+    for (int32_t j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < dk; ++c) acc += kk[c] * a[c] * S[c * dv + j];
+      u[j] -= acc;
+    }
+#else
+    /* S' = Diag(alpha) S: scale row c (key channel c) by alpha_c */
+#if KDA_ORACLE_MUTANT == 1 || KDA_ORACLE_MUTANT == 8
+    /* mistake: decay dropped here (mutant 8 applies it after the write) */
+#else
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= a[c];
+#endif
+    /* u = v - S'^T k */
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j)
+#if KDA_ORACLE_MUTANT == 3
+        u[j] += S[c * dv + j] * kk[c]; /* mistake: sign of the residual */
+#else
+        u[j] -= S[c * dv + j] * kk[c];
+#endif
+#endif
+    /* S = S' + beta k u^T */
+    for (int32_t c = 0; c < dk; ++c) {
+#if KDA_ORACLE_MUTANT == 7
+      const double bk = kk[c]; /* mistake: beta dropped from the write */
+#else
+      const double bk = b * kk[c];
+#endif
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] += bk * u[j];
+    }
+#if KDA_ORACLE_MUTANT == 8
+    /* mistake: decay applied after the delta-rule write */
+    for (int32_t c = 0; c < dk; ++c)
+      for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= a[c];
+#endif
+    /* o = S^T q (read after write) */
+#if KDA_ORACLE_MUTANT != 2
+    if (o) {
+      double* orow = o + ((bos + t) * n_sel + hs) * dv;
+      for (int32_t j = 0; j < dv; ++j) orow[j] = 0.0;
+#if KDA_ORACLE_MUTANT == 4
+      /* mistake: the state is read with the key instead of the query */
+      for (int32_t c = 0; c < dk; ++c)
+        for (int32_t j = 0; j < dv; ++j) orow[j] += S[c * dv + j] * kk[c];
+#else
+      for (int32_t c = 0; c < dk; ++c)
+        for (int32_t j = 0; j < dv; ++j) orow[j] += S[c * dv + j] * qq[c];
+#endif
+    }
+#endif
+    /* checkpoint: state after P tokens */
+#if KDA_ORACLE_MUTANT == 6
+    const int64_t p_now = st + t + 2; /* mistake: off by one token */
+#else
+    const int64_t p_now = st + t + 1;
+#endif
+    if (m < m_end && ckpt_pos[m] == p_now) {
+      memcpy(ckpt_out + ((int64_t)m * n_sel + hs) * SD, S, sizeof(double) * SD);
+      ++m;
+    }
+  }
+  if (s_final) memcpy(s_final + ((int64_t)s * n_sel + hs) * SD, S, sizeof(double) * SD);
+}
+
 /*
  * Layouts (T = cu_seqlens[num_seqs]):
  *   q, k, gate : [T][H][dk]     v : [T][H][dv]     beta : [T][H]
@@ -124,101 +230,11 @@ int kda_oracle_run(int32_t H, int32_t dk, int32_t dv, int32_t num_seqs, const in
       const int32_t h = heads ? heads[hs] : hs;
       const int64_t bos = cu_seqlens[s], len = cu_seqlens[s + 1] - bos;
       const int64_t st = start_pos ? start_pos[s] : 0;
-      int32_t m = ckpt_cu ? ckpt_cu[s] : 0;
+      const int32_t m = ckpt_cu ? ckpt_cu[s] : 0;
       const int32_t m_end = ckpt_cu ? ckpt_cu[s + 1] : 0;
 
-      if (s0)
-        memcpy(S, s0 + ((int64_t)s * n_sel + hs) * SD, sizeof(double) * SD);
-      else
-        memset(S, 0, sizeof(double) * SD);
-
-      for (int64_t t = 0; t < len; ++t) {
-        const int64_t row = (bos + t) * H + h; /* (token, head) row index */
-        const double b = ld(beta, in_dtype, row);
-        for (int32_t c = 0; c < dk; ++c) {
-          const double gv = ld(gate, in_dtype, row * dk + c);
-          a[c] = gate_is_alpha ? gv : exp(gv);
-          kk[c] = ld(k, in_dtype, row * dk + c);
-          qq[c] = ld(q, in_dtype, row * dk + c);
-        }
-        for (int32_t j = 0; j < dv; ++j) u[j] = ld(v, in_dtype, row * dv + j);
-
-#if KDA_ORACLE_MUTANT == 2
-        /* mistake: read before this token's update */
-        if (o) {
-          double* orow = o + ((bos + t) * n_sel + hs) * dv;
-          for (int32_t j = 0; j < dv; ++j) orow[j] = 0.0;
-          for (int32_t c = 0; c < dk; ++c)
-            for (int32_t j = 0; j < dv; ++j) orow[j] += S[c * dv + j] * qq[c];
-        }
-#endif
-
-#if KDA_ORACLE_MUTANT == 5
-        /* mistake: literal bracket reading, decay only inside the erase term:
-           S <- S - beta k (k^T Diag(a) S) + beta k v^T */
-        for (int32_t j = 0; j < dv; ++j) {
-          double acc = 0.0;
-          for (int32_t c = 0; c < dk; ++c) acc += kk[c] * a[c] * S[c * dv + j];
-          u[j] -= acc;
-        }
-#else
-        /* S' = Diag(alpha) S: scale row c (key channel c) by alpha_c */
-#if KDA_ORACLE_MUTANT == 1 || KDA_ORACLE_MUTANT == 8
-        /* mistake: decay dropped here (mutant 8 applies it after the write) */
-#else
-        for (int32_t c = 0; c < dk; ++c)
-          for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= a[c];
-#endif
-        /* u = v - S'^T k */
-        for (int32_t c = 0; c < dk; ++c)
-          for (int32_t j = 0; j < dv; ++j)
-#if KDA_ORACLE_MUTANT == 3
-            u[j] += S[c * dv + j] * kk[c]; /* mistake: sign of the residual */
-#else
-            u[j] -= S[c * dv + j] * kk[c];
-#endif
-#endif
-        /* S = S' + beta k u^T */
-        for (int32_t c = 0; c < dk; ++c) {
-#if KDA_ORACLE_MUTANT == 7
-          const double bk = kk[c]; /* mistake: beta dropped from the write */
-#else
-          const double bk = b * kk[c];
-#endif
-          for (int32_t j = 0; j < dv; ++j) S[c * dv + j] += bk * u[j];
-        }
-#if KDA_ORACLE_MUTANT == 8
-        /* mistake: decay applied after the delta-rule write */
-        for (int32_t c = 0; c < dk; ++c)
-          for (int32_t j = 0; j < dv; ++j) S[c * dv + j] *= a[c];
-#endif
-        /* o = S^T q (read after write) */
-#if KDA_ORACLE_MUTANT != 2
-        if (o) {
-          double* orow = o + ((bos + t) * n_sel + hs) * dv;
-          for (int32_t j = 0; j < dv; ++j) orow[j] = 0.0;
-#if KDA_ORACLE_MUTANT == 4
-          /* mistake: the state is read with the key instead of the query */
-          for (int32_t c = 0; c < dk; ++c)
-            for (int32_t j = 0; j < dv; ++j) orow[j] += S[c * dv + j] * kk[c];
-#else
-          for (int32_t c = 0; c < dk; ++c)
-            for (int32_t j = 0; j < dv; ++j) orow[j] += S[c * dv + j] * qq[c];
-#endif
-        }
-#endif
-        /* checkpoint: state after P tokens */
-#if KDA_ORACLE_MUTANT == 6
-        const int64_t p_now = st + t + 2; /* mistake: off by one token */
-#else
-        const int64_t p_now = st + t + 1;
-#endif
-        if (m < m_end && ckpt_pos[m] == p_now) {
-          memcpy(ckpt_out + ((int64_t)m * n_sel + hs) * SD, S, sizeof(double) * SD);
-          ++m;
-        }
-      }
-      if (s_final) memcpy(s_final + ((int64_t)s * n_sel + hs) * SD, S, sizeof(double) * SD);
+      run_pair(H, dk, dv, in_dtype, gate_is_alpha, q, k, v, gate, beta, s0, o, s_final, ckpt_pos,
+               ckpt_out, n_sel, s, hs, h, bos, len, st, m, m_end, S, u, a, kk, qq);
     }
     free(S);
     free(u);

@@ -1,0 +1,201 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, computes pool offsets, and rejects bad arguments with
+the documented status before touching the device (all-or-nothing).
+
+Device pointers below are fake aligned integers: every call here fails
+validation, so none of them is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import hybrid_prefix_cache_amd as K
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kda.h")
+FAKE = 1 << 20  # 256-byte aligned, never dereferenced
+MiB2 = 2 << 20
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"kda_prefill_chunked", "kda_decode_step", "kda_checkpoint_write",
+                          "kda_checkpoint_restore"}
+    lib = ctypes.CDLL(K.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+    assert set(names) == set(K.EXPORTS)
+
+
+def pool(**kw):
+    d = dict(base=FAKE, page_bytes=MiB2, num_pages=16, num_heads=32, d_k=128)
+    d.update(kw)
+    return K.make_pool(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, K.KDA_OK),
+    (dict(base=0), K.KDA_ERR_POOL),
+    (dict(base=FAKE + 16), K.KDA_ERR_POOL),
+    (dict(d_k=96), K.KDA_ERR_SHAPE),
+    (dict(d_k=128, d_v=64), K.KDA_ERR_SHAPE),
+    (dict(page_bytes=MiB2 - 256), K.KDA_ERR_POOL),   # smaller than 32 heads x 64 KiB
+    (dict(page_bytes=MiB2 + 8), K.KDA_ERR_POOL),     # not a multiple of 256
+    (dict(page_bytes=MiB2 + 4096), K.KDA_OK),
+    (dict(num_pages=0), K.KDA_ERR_POOL),
+    (dict(num_heads=0), K.KDA_ERR_POOL),
+])
+def test_pool_check(kw, status):
+    assert K.kda_pool_check(pool(**kw)) == status
+    if status != K.KDA_OK:
+        assert K.kda_last_error() != ""
+    else:
+        assert K.kda_last_error() == ""
+
+
+def test_pool_check_null():
+    assert K.raw_call("kda_pool_check", None) == K.KDA_ERR_NULL
+
+
+def test_state_offset_layout():
+    # heads stored contiguously inside a page; pages of a fixed byte size
+    p = pool(page_bytes=MiB2 + 4096, num_pages=8, num_heads=32, d_k=128)
+    for page in (0, 1, 7):
+        for head in (0, 1, 31):
+            assert K.kda_state_offset(p, page, head) == page * (MiB2 + 4096) + head * 128 * 128 * 4
+    assert K.kda_state_offset(p, 8, 0) == -1
+    assert K.kda_state_offset(p, 0, 32) == -1
+    assert K.kda_state_offset(p, -1, 0) == -1
+    p64 = pool(num_heads=1, d_k=64, page_bytes=16384, num_pages=4)
+    assert K.kda_state_offset(p64, 3, 0) == 3 * 16384
+
+
+def test_workspace_bytes():
+    p = pool()
+    a = K.kda_prefill_workspace_bytes(p, 8192, 1, 3, K.KDA_BF16)
+    b = K.kda_prefill_workspace_bytes(p, 8192, 1, 3, K.KDA_F32)
+    assert a > 0 and b > a
+    # per (chunk, head): 3 x [64][128] + 2 x [64][64] elements + fp32 gamma, 256-aligned
+    blk = ((3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128 + 255) // 256 * 256
+    assert a >= (8192 // 64) * 32 * blk
+    assert K.kda_prefill_workspace_bytes(p, 8192, 2, 3, K.KDA_BF16) > a
+    assert K.kda_prefill_workspace_bytes(p, -1, 1, 0, K.KDA_BF16) == 0
+    assert K.kda_prefill_workspace_bytes(p, 10, 1, 0, 7) == 0
+
+
+def _prefill_status(p=None, T=1024, **kw):
+    """Call kda_prefill_chunked with fake device pointers; returns the status."""
+    p = p or pool()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, cu_seqlens=[0, T],
+                in_dtype=K.KDA_BF16, out_dtype=K.KDA_BF16, workspace=FAKE,
+                workspace_bytes=1 << 40, stream=0)
+    args.update(kw)
+    try:
+        K.kda_prefill_chunked(p, **args)
+    except K.KdaError as e:
+        assert K.kda_last_error() != ""
+        return e.status
+    return K.KDA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk_size=32), K.KDA_ERR_SHAPE),
+    (dict(hash_block=500), K.KDA_ERR_SHAPE),
+    (dict(hash_block=0), K.KDA_ERR_SHAPE),
+    (dict(in_dtype=5), K.KDA_ERR_DTYPE),
+    (dict(out_dtype=-1), K.KDA_ERR_DTYPE),
+    (dict(cu_seqlens=[1, 1024]), K.KDA_ERR_SEQ),
+    (dict(cu_seqlens=[0, 512, 256]), K.KDA_ERR_SEQ),
+    (dict(start_pos=[100]), K.KDA_ERR_SEQ),
+    (dict(start_pos=[-64]), K.KDA_ERR_SEQ),
+    (dict(q=0), K.KDA_ERR_NULL),
+    (dict(o=0), K.KDA_ERR_NULL),
+    (dict(q=FAKE + 8), K.KDA_ERR_SHAPE),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[500], ckpt_page=[3]), K.KDA_ERR_CKPT_ALIGN),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[1536], ckpt_page=[3]), K.KDA_ERR_CKPT_RANGE),
+    (dict(ckpt_cu=[0, 2], ckpt_pos=[1024, 512], ckpt_page=[3, 4]), K.KDA_ERR_CKPT_RANGE),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[0], ckpt_page=[3]), K.KDA_ERR_CKPT_RANGE),
+    (dict(start_pos=[512], ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[3]), K.KDA_ERR_CKPT_RANGE),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[16]), K.KDA_ERR_PAGE_RANGE),
+    (dict(state_in_page=[16]), K.KDA_ERR_PAGE_RANGE),
+    (dict(state_out_page=[-2]), K.KDA_ERR_PAGE_RANGE),
+    (dict(ckpt_cu=[0, 2], ckpt_pos=[512, 1024], ckpt_page=[3, 3]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(state_out_page=[3], ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[3]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(state_in_page=[3], ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[3]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(cu_seqlens=[0, 512, 1024], state_in_page=[2, -1], state_out_page=[-1, 2]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(cu_seqlens=[0, 512, 1024], state_out_page=[5, 5]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(cu_seqlens=[0, 512, 1024], state_in_page=[5, 5], state_out_page=[5, -1]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(workspace=0), K.KDA_ERR_WORKSPACE),
+    (dict(workspace=FAKE + 64), K.KDA_ERR_WORKSPACE),
+    (dict(workspace_bytes=1024), K.KDA_ERR_WORKSPACE),
+])
+def test_prefill_validation(kw, status):
+    assert _prefill_status(**kw) == status
+
+
+def test_prefill_rejects_bad_pool_and_accepts_empty_batch():
+    assert _prefill_status(p=pool(d_k=32)) == K.KDA_ERR_SHAPE
+    # zero sequences: nothing to do, nothing enqueued
+    st = K.raw_call("kda_prefill_chunked", ctypes.byref(pool()), None, None, None, None, None,
+                    K.KDA_BF16, None, K.KDA_BF16, 0, None, None, None, None, None, None, None,
+                    64, 512, None, 0, None)
+    assert st == K.KDA_OK
+
+
+def test_workspace_bound_matches_check():
+    """The size kda_prefill_workspace_bytes reports is accepted; one byte less
+    than the exact need is rejected (varlen, partial chunks)."""
+    p = pool()
+    cu = [0, 100, 100, 1000, 1100]
+    need = K.kda_prefill_workspace_bytes(p, 1100, 4, 0, K.KDA_BF16)
+    chunks = sum((b - a + 63) // 64 for a, b in zip(cu[:-1], cu[1:]))
+    blk = ((3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128 + 255) // 256 * 256
+    exact_inter = chunks * 32 * blk
+    assert need >= exact_inter
+    assert _prefill_status(p=p, cu_seqlens=cu, workspace_bytes=exact_inter - 1) == K.KDA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("fn", ["kda_checkpoint_write", "kda_checkpoint_restore"])
+@pytest.mark.parametrize("src,dst,status", [
+    ([1, 2], [3, 16], K.KDA_ERR_PAGE_RANGE),
+    ([-1], [3], K.KDA_ERR_PAGE_RANGE),
+    ([1, 2], [3, 3], K.KDA_ERR_PAGE_ALIAS),
+    ([1, 2], [2, 4], K.KDA_ERR_PAGE_ALIAS),
+    ([5], [5], K.KDA_ERR_PAGE_ALIAS),
+])
+def test_copy_validation(fn, src, dst, status):
+    with pytest.raises(K.KdaError) as ei:
+        getattr(K, fn)(pool(), src, dst, stream=0)
+    assert ei.value.status == status
+
+
+def test_copy_empty_is_noop():
+    K.kda_checkpoint_write(pool(), [], [], stream=0)
+
+
+def test_decode_validation():
+    p = pool()
+    st = K.raw_call("kda_decode_step", ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, K.KDA_BF16,
+                    FAKE, K.KDA_BF16, -1, FAKE, FAKE, None)
+    assert st == K.KDA_ERR_SHAPE
+    st = K.raw_call("kda_decode_step", ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, K.KDA_BF16,
+                    FAKE, K.KDA_BF16, 4, None, FAKE, None)
+    assert st == K.KDA_ERR_NULL
+    st = K.raw_call("kda_decode_step", ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 3,
+                    FAKE, K.KDA_BF16, 4, FAKE, FAKE, None)
+    assert st == K.KDA_ERR_DTYPE
+    st = K.raw_call("kda_decode_step", ctypes.byref(p), None, None, None, None, None, K.KDA_BF16,
+                    None, K.KDA_BF16, 0, None, None, None)
+    assert st == K.KDA_OK  # n = 0: nothing to do
+
+
+def test_version():
+    assert K.kda_version() >> 16 >= 1

@@ -1,0 +1,226 @@
+"""GPU prefill parity: libkda (HIP, gfx950) vs the fp64 oracle, through the C ABI.
+
+Bar: max relative Frobenius error (per (sequence, head) block of o, per
+checkpointed / final state) <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs;
+checkpoint placement and page indexing bit-exact (poisoned pool: exactly the
+designated state bytes change); repeated runs and resumed runs bitwise equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_prefix_cache_amd as K
+import kda_inputs as G
+import oracle
+from kda_gpu_util import (POISON_WORD, PoolBuf, inputs_to_dev, max_rel_blocks, prefill,
+                          rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _poison_mask_ok(before, after, pb, changed_pages):
+    """Only the state bytes of `changed_pages` may differ; everything else keeps
+    its previous bytes (page padding included)."""
+    w = pb.page_bytes // 4
+    sw = pb.state_bytes // 4
+    allowed = np.zeros(before.shape, bool)
+    for p in changed_pages:
+        allowed[p * w:p * w + sw] = True
+    if np.any(before[~allowed] != after[~allowed]):
+        return False
+    # every designated word was written (no poison left behind)
+    for p in changed_pages:
+        if np.any(after[p * w:p * w + sw] == np.int32(np.uint32(POISON_WORD).view(np.int32))):
+            return False
+    return True
+
+
+def _oracle_prefill(d, cu, **kw):
+    return oracle.run(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, **kw)
+
+
+# ---------------------------------------------------------------------------
+def test_single_1k_f32():
+    """One sequence, H=1, d=64, T=1024, fp32, S0 = 0, checkpoints at 512 and 1024."""
+    w = G.SINGLE_1K
+    d = G.kda_tokens(w.seed, w.H, w.D, 0, w.T, w.dtype)
+    pb = PoolBuf(4, w.H, w.D)
+    before = pb.snapshot()
+    o = prefill(pb, inputs_to_dev(d, w.dtype), [0, w.T], w.dtype, ckpt_cu=[0, 2],
+                ckpt_pos=list(w.ckpts), ckpt_page=[1, 2], state_out_page=[3])
+    ref = _oracle_prefill(d, [0, w.T], ckpt_cu=[0, 2], ckpt_pos=list(w.ckpts))
+    err_o = max_rel_blocks(o.double().cpu().numpy(), ref["o"], [0, w.T], w.H)
+    err_c = max(rel_fro(pb.states(1 + m)[0], ref["ckpts"][m, 0]) for m in range(2))
+    assert err_o <= TOL["f32"] and err_c <= TOL["f32"], (err_o, err_c)
+    assert np.array_equal(pb.states(2), pb.states(3))  # checkpoint at T == final state
+    assert _poison_mask_ok(before, pb.snapshot(), pb, [1, 2, 3])
+
+
+@pytest.mark.parametrize("dtype,D,H,cu", [
+    ("bf16", 128, 4, [0, 1000]),                      # ragged tail (1000 = 15*64 + 40)
+    ("bf16", 64, 3, [0, 700]),
+    ("f32", 128, 2, [0, 300]),
+    ("f32", 64, 2, [0, 130, 130, 200, 777]),          # varlen with an empty sequence
+    ("bf16", 128, 2, [0, 1, 65, 129, 700, 1212]),     # 1-token and 64-token sequences
+])
+def test_small_cases(dtype, D, H, cu):
+    T = cu[-1]
+    d = G.kda_tokens(1234 + D + H, H, D, 0, T, dtype)
+    ns = len(cu) - 1
+    pb = PoolBuf(2 * ns + 2, H, D)
+    out_pages = list(range(ns))
+    o = prefill(pb, inputs_to_dev(d, dtype), cu, dtype, state_out_page=out_pages)
+    ref = _oracle_prefill(d, cu)
+    err_o = max_rel_blocks(o.double().cpu().numpy(), ref["o"], cu, H)
+    err_s = max(rel_fro(pb.states(s)[h], ref["s_final"][s, h]) if cu[s + 1] > cu[s] else 0.0
+                for s in range(ns) for h in range(H))
+    assert err_o <= TOL[dtype] and err_s <= TOL[dtype], (err_o, err_s)
+    for s in range(ns):  # empty sequence with no entering state: zero final state
+        if cu[s + 1] == cu[s]:
+            assert np.all(pb.states(s) == 0)
+
+
+@pytest.mark.parametrize("page_bytes", [2 << 20, (2 << 20) + 4096])
+def test_prefill_8k_full(page_bytes):
+    """H=32, d=128, T=8192, bf16 inputs, fp32 state, checkpoints {2560, 6144, 8192}
+    into 2 MiB pages (and a padded page size); all heads checked."""
+    w = G.PREFILL_8K
+    d = G.kda_tokens(w.seed, w.H, w.D, 0, w.T, w.dtype)
+    pb = PoolBuf(8, w.H, w.D, page_bytes=page_bytes)
+    ck_pages = [5, 2, 7]
+    before = pb.snapshot()
+    di = inputs_to_dev(d, w.dtype)
+    kw = dict(ckpt_cu=[0, 3], ckpt_pos=list(w.ckpts), ckpt_page=ck_pages, state_out_page=[0])
+    o = prefill(pb, di, [0, w.T], w.dtype, **kw)
+    after = pb.snapshot()
+    ref = _oracle_prefill(d, [0, w.T], ckpt_cu=[0, 3], ckpt_pos=list(w.ckpts))
+    err_o = max_rel_blocks(o.double().cpu().numpy(), ref["o"], [0, w.T], w.H)
+    err_c = max(rel_fro(pb.states(p)[h], ref["ckpts"][m, h])
+                for m, p in enumerate(ck_pages) for h in range(w.H))
+    assert err_o <= TOL["bf16"] and err_c <= TOL["bf16"], (err_o, err_c)
+    assert _poison_mask_ok(before, after, pb, ck_pages + [0])
+    assert np.array_equal(pb.states(7), pb.states(0))  # checkpoint at T == final state
+    # determinism: a second run gives bitwise-identical outputs and pages
+    o2 = prefill(pb, di, [0, w.T], w.dtype, **kw)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert np.array_equal(after, pb.snapshot())
+
+
+@pytest.mark.parametrize("g_lo", [-0.05, -0.001])
+def test_resume_bitwise_and_oracle(g_lo):
+    """Prefill [0, B) with a checkpoint at B, restore it into a fresh active page,
+    prefill [B, T) from it: bitwise equal to the uninterrupted GPU run, and both
+    match the oracle.  The slow-decay variant keeps a wrong restore visible long
+    after B."""
+    H, D, T, B = 8, 128, 3000, 1536
+    d = G.kda_tokens(777, H, D, 0, T, "bf16", g_lo=g_lo)
+    di = inputs_to_dev(d, "bf16")
+    pb = PoolBuf(8, H, D)
+    o_full = prefill(pb, di, [0, T], "bf16", ckpt_cu=[0, 1], ckpt_pos=[B], ckpt_page=[1],
+                     state_out_page=[2])
+    pre = {k: v[:B] for k, v in di.items()}
+    suf = {k: v[B:].contiguous() for k, v in di.items()}
+    o_pre = prefill(pb, pre, [0, B], "bf16", ckpt_cu=[0, 1], ckpt_pos=[B], ckpt_page=[3])
+    ck_bytes = pb.page_words(3).clone()
+    K.kda_checkpoint_restore(pb.pool, [3], [4])
+    o_suf = prefill(pb, suf, [0, T - B], "bf16", start_pos=[B], state_in_page=[4],
+                    state_out_page=[5])
+    assert torch.equal(pb.page_words(3), ck_bytes)  # checkpoint stayed read-only
+    assert torch.equal(o_full[:B].view(torch.int16), o_pre.view(torch.int16))
+    assert torch.equal(o_full[B:].view(torch.int16), o_suf.view(torch.int16))
+    assert np.array_equal(pb.states(1), pb.states(3))
+    assert np.array_equal(pb.states(2), pb.states(5))
+    ref = _oracle_prefill(d, [0, T], ckpt_cu=[0, 1], ckpt_pos=[B])
+    err = max(max_rel_blocks(o_full.double().cpu().numpy(), ref["o"], [0, T], H),
+              max(rel_fro(pb.states(1)[h], ref["ckpts"][0, h]) for h in range(H)),
+              max(rel_fro(pb.states(2)[h], ref["s_final"][0, h]) for h in range(H)))
+    assert err <= TOL["bf16"], err
+
+
+def test_in_place_and_empty_sequence_with_state():
+    """state_in == state_out updates in place; a zero-length sequence with an
+    entering state copies it to its output page unchanged."""
+    H, D = 4, 64
+    cu = [0, 640, 640]
+    d = G.kda_tokens(99, H, D, 0, 640, "f32")
+    pb = PoolBuf(6, H, D)
+    rng = np.random.default_rng(5)
+    s0 = rng.standard_normal((2, H, D, D)) / np.sqrt(D)
+    pb.set_states(1, s0[0])
+    pb.set_states(2, s0[1])
+    o = prefill(pb, inputs_to_dev(d, "f32"), cu, "f32", start_pos=[1024, 4096],
+                state_in_page=[1, 2], state_out_page=[1, 3],
+                ckpt_cu=[0, 1, 1], ckpt_pos=[1536], ckpt_page=[4])
+    s0_f32 = s0.astype(np.float32).astype(np.float64)
+    ref = _oracle_prefill(d, cu, start_pos=[1024, 4096], s0=s0_f32, ckpt_cu=[0, 1, 1],
+                          ckpt_pos=[1536])
+    assert max_rel_blocks(o.double().cpu().numpy(), ref["o"], cu, H) <= 1e-4
+    assert max(rel_fro(pb.states(1)[h], ref["s_final"][0, h]) for h in range(H)) <= 1e-4
+    assert max(rel_fro(pb.states(4)[h], ref["ckpts"][0, h]) for h in range(H)) <= 1e-4
+    assert np.array_equal(pb.states(3), s0_f32)
+
+
+def test_varlen_resume_batch():
+    """16 sequences, lengths uniform in [1024, 32768]; each resumes from a
+    checkpoint at a random 512-multiple B < len.  Prefix pass writes the
+    checkpoints, restore copies them to fresh active pages, the packed suffix
+    pass resumes.  Checked against the uninterrupted oracle on sampled heads."""
+    w = G.VARLEN_RESUME
+    lens, bnd = G.varlen_plan(w)
+    ns, H, D = w.n_seqs, w.H, w.D
+    seqs = [G.kda_tokens(w.seed, H, D, 0, int(L), w.dtype, seq_id=s) for s, L in enumerate(lens)]
+    cat = lambda parts: np.concatenate(parts, axis=0)  # noqa: E731
+    pre = {k: cat([sq[k][:b] for sq, b in zip(seqs, bnd)]) for k in seqs[0]}
+    suf = {k: cat([sq[k][b:] for sq, b in zip(seqs, bnd)]) for k in seqs[0]}
+    cu_pre = np.concatenate([[0], np.cumsum(bnd)])
+    cu_suf = np.concatenate([[0], np.cumsum(lens - bnd)])
+    pb = PoolBuf(3 * ns, H, D, page_bytes=2 << 20)
+    ck_pages = list(range(ns))
+    act_pages = list(range(ns, 2 * ns))
+    fin_pages = list(range(2 * ns, 3 * ns))
+    prefill(pb, inputs_to_dev(pre, "bf16"), cu_pre, "bf16", ckpt_cu=np.arange(ns + 1),
+            ckpt_pos=bnd, ckpt_page=ck_pages)
+    K.kda_checkpoint_restore(pb.pool, ck_pages, act_pages)
+    o_suf = prefill(pb, inputs_to_dev(suf, "bf16"), cu_suf, "bf16", start_pos=bnd,
+                    state_in_page=act_pages, state_out_page=fin_pages)
+    o_suf = o_suf.double().cpu().numpy()
+    heads = [0, 13, 31]
+    full = {k: cat([sq[k] for sq in seqs]) for k in seqs[0]}
+    cu_full = np.concatenate([[0], np.cumsum(lens)])
+    ref = _oracle_prefill(full, cu_full, ckpt_cu=np.arange(ns + 1), ckpt_pos=bnd, heads=heads)
+    worst = 0.0
+    for s in range(ns):
+        a, b = int(cu_full[s]) + int(bnd[s]), int(cu_full[s + 1])
+        sa, sb = int(cu_suf[s]), int(cu_suf[s + 1])
+        for j, h in enumerate(heads):
+            worst = max(worst, rel_fro(o_suf[sa:sb, h], ref["o"][a:b, j]),
+                        rel_fro(pb.states(ck_pages[s])[h], ref["ckpts"][s, j]),
+                        rel_fro(pb.states(fin_pages[s])[h], ref["s_final"][s, j]))
+    assert worst <= TOL["bf16"], worst
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_long_1m():
+    """T = 2^20 tokens, H=32, d=128, bf16, 171 checkpoints streamed to the pool.
+    The oracle runs one full head (all tokens, all checkpoints); every head's
+    checkpoints must be finite and distinct from the poison."""
+    w = G.LONG_1M
+    d = G.kda_tokens(w.seed, w.H, w.D, 0, w.T, w.dtype)
+    di = inputs_to_dev(d, w.dtype)
+    nck = len(w.ckpts)
+    pb = PoolBuf(nck + 1, w.H, w.D, page_bytes=w.page_bytes)
+    o = prefill(pb, di, [0, w.T], w.dtype, ckpt_cu=[0, nck], ckpt_pos=list(w.ckpts),
+                ckpt_page=list(range(nck)), state_out_page=[nck])
+    del di
+    heads = [5]
+    ref = _oracle_prefill(d, [0, w.T], ckpt_cu=[0, nck], ckpt_pos=list(w.ckpts), heads=heads)
+    o_h = o[:, heads[0]].double().cpu().numpy()
+    err_o = rel_fro(o_h, ref["o"][:, 0])
+    err_c = max(rel_fro(pb.states(m)[heads[0]], ref["ckpts"][m, 0]) for m in range(nck))
+    assert err_o <= TOL["bf16"] and err_c <= TOL["bf16"], (err_o, err_c)
+    assert np.array_equal(pb.states(nck - 1), pb.states(nck))
+    for m in range(0, nck, 17):
+        assert np.all(np.isfinite(pb.states(m)))
