@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+A step is one kda_prefill_chunked call over the 8K workload (H=32, d=128,
+T=8192, bf16 inputs, fp32 state, checkpoints at {2560, 6144, 8192} written into
+a pool of 2 MiB pages): metadata tables, the state-independent chunk products,
+the state scan and the fused checkpoint / final-state stores.  The same run
+also times the decode step (256 requests x 32 heads, in place through a page
+table) and the checkpoint page copies (256 x 2 MiB pages), and reports them
+under "decode" and "checkpoint_copy".  Inputs are synthetic (seeded Philox
+generators) and resident in HBM before timing starts.
+
+Prints ONE JSON line (see the "roofline" and "cpu_baseline" fields).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/sec (H=32,d=128) + decode GB/s; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+# Algorithmic work per (token, head) of prefill at chunk C=64, d=128, bf16 I/O:
+#   bytes: q, k, v, g (4 x d x 2) + beta (2) + o (d x 2) = 1282
+#   flops: 4*C*d + 6*d^2 = 131072
+# plus 64 KiB per (checkpoint, head) stored.
+PREFILL_BYTES_PER_TOKEN_HEAD = 1282
+PREFILL_FLOPS_PER_TOKEN_HEAD = 131072
+# split of the per-(token, head) bytes between the two prefill kernels:
+#   prep reads q, k, g, beta; scan reads v, writes o and the state pages
+PREP_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 2
+SCAN_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(x, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+
+
+def timed(fn, steps, warmup):
+    """Run fn warmup times, then time exactly `steps` calls between two device
+    synchronisations (HIP events on the current stream + host clock)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def kernel_times(K, fn, reps):
+    """Average per-launch duration of every library kernel over `reps` calls,
+    from HIP events the library records around each launch on its stream."""
+    import torch
+    torch.cuda.synchronize()
+    K.kda_profile_read(reset=True)
+    K.kda_profile_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    K.kda_profile_enable(False)
+    stats = K.kda_profile_read(reset=True)
+    return {name: {"launches": n, "avg_ms": ms / max(n, 1)} for name, (n, ms) in stats.items()}
+
+
+def bench_prefill(K, G, steps, warmup):
+    import torch
+    w = G.PREFILL_8K
+    d = G.kda_tokens(w.seed, w.H, w.D, 0, w.T, w.dtype)
+    di = {k: to_dev(v, w.dtype) for k, v in d.items()}
+    num_pages = 8
+    pool_buf = torch.zeros(num_pages * w.page_bytes // 4, dtype=torch.int32, device="cuda")
+    pool = K.make_pool(pool_buf, w.page_bytes, num_pages, w.H, w.D)
+    o = torch.empty((w.T, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_bytes(pool, w.T, 1, len(w.ckpts), K.KDA_BF16),
+                     dtype=torch.uint8, device="cuda")
+    kw = dict(ckpt_cu=[0, len(w.ckpts)], ckpt_pos=list(w.ckpts), ckpt_page=[1, 2, 3],
+              state_out_page=[0], workspace=ws)
+
+    def step():
+        K.kda_prefill_chunked(pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, [0, w.T], **kw)
+
+    dev_s, wall_s = timed(step, steps, warmup)
+    kt = kernel_times(K, step, max(steps, 5))
+    return w, d, dev_s, wall_s, kt
+
+
+def bench_decode(K, G, steps, warmup, n_inputs=32):
+    import torch
+    w = G.DECODE_256
+    pt = torch.from_numpy(G.decode_page_table(w)).cuda()
+    pool_buf = torch.zeros(w.pool_pages * w.page_bytes // 4, dtype=torch.int32, device="cuda")
+    s0 = G.random_states(w.seed, w.n_req, w.H, w.D)
+    words = w.page_bytes // 4
+    sb = w.H * w.D * w.D
+    for r, p in enumerate(pt.cpu().numpy()):
+        pool_buf[p * words:p * words + sb] = torch.from_numpy(s0[r].reshape(-1)).cuda().view(torch.int32)
+    pool = K.make_pool(pool_buf, w.page_bytes, w.pool_pages, w.H, w.D)
+    d = G.kda_tokens(w.seed, w.H, w.D, 0, n_inputs * w.n_req, w.dtype)
+    di = {k: to_dev(v, w.dtype) for k, v in d.items()}
+    o = torch.empty((w.n_req, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    it = [0]
+
+    def step():
+        i = it[0] % n_inputs
+        it[0] += 1
+        sl = slice(i * w.n_req, (i + 1) * w.n_req)
+        K.kda_decode_step(pool, di["q"][sl], di["k"][sl], di["v"][sl], di["g"][sl], di["beta"][sl],
+                          o, pt, pt)
+
+    dev_s, wall_s = timed(step, steps, warmup)
+    kt = kernel_times(K, step, 50)
+    state_bytes = 2 * w.n_req * w.H * w.D * w.D * 4           # read + write
+    io_bytes = w.n_req * w.H * (4 * w.D * 2 + 2 + w.D * 2)     # q,k,v,g,beta in; o out
+    per_step = state_bytes + io_bytes
+    avg = kt["kda_decode_step"]["avg_ms"] / 1e3
+    return {
+        "workload": w.name, "steps": steps, "distinct_input_sets": n_inputs,
+        "ms_per_step": 1e3 * dev_s / steps, "bytes_per_step": per_step,
+        "gbps": per_step / (dev_s / steps) / 1e9,
+        "kernel_avg_ms": 1e3 * avg, "kernel_gbps": per_step / avg / 1e9,
+        "frac_hbm": per_step / avg / 1e9 / HBM_PEAK_GBS,
+        "tokens_per_s": w.n_req * steps / dev_s,
+    }
+
+
+def bench_copy(K, steps, warmup):
+    import torch
+    H, D, page_bytes, n = 32, 128, 2 << 20, 256
+    pool_buf = torch.zeros(2 * n * page_bytes // 4, dtype=torch.int32, device="cuda")
+    pool = K.make_pool(pool_buf, page_bytes, 2 * n, H, D)
+    src, dst = list(range(n)), list(range(n, 2 * n))
+
+    def step():
+        K.kda_checkpoint_write(pool, src, dst)
+
+    dev_s, _ = timed(step, steps, warmup)
+    kt = kernel_times(K, step, 20)
+    moved = 2 * n * H * D * D * 4
+    avg = kt["kda_page_copy"]["avg_ms"] / 1e3
+    return {"pages": n, "page_bytes": page_bytes, "bytes_per_call": moved,
+            "ms_per_call": 1e3 * dev_s / steps, "gbps": moved / (dev_s / steps) / 1e9,
+            "kernel_avg_ms": 1e3 * avg, "kernel_gbps": moved / avg / 1e9,
+            "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(G, w, d):
+    """The fp64 oracle on the same 8K workload (all 32 heads, all tokens), timed on
+    this host's cores.  Generation is excluded."""
+    import oracle
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.run(d["q"], d["k"], d["v"], d["g"], d["beta"], [0, w.T], ckpt_cu=[0, len(w.ckpts)],
+               ckpt_pos=list(w.ckpts), threads=threads)
+    el = time.perf_counter() - t0
+    return {"value": w.T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload: {w.T} tokens x {w.H} heads, fp64 token loop, "
+                      f"{el:.2f} s, OpenMP over heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_prefix_cache_amd as K
+    import kda_inputs as G
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    log("prefill: generating inputs")
+    w, d, dev_s, wall_s, kt = bench_prefill(K, G, args.steps, args.warmup)
+    ms_step = 1e3 * dev_s / args.steps
+    tok_s = w.T * args.steps / dev_s
+    log(f"prefill: {ms_step:.3f} ms/step, {tok_s / 1e6:.2f} M tokens/s; kernels {kt}")
+
+    # roofline of the dominant kernel (HBM-bound, algorithmic bytes per launch)
+    th = w.T * w.H
+    ck_bytes = len(w.ckpts) * w.H * w.D * w.D * 4 + w.H * w.D * w.D * 4  # checkpoints + final state
+    alg = {"kda_prefill_prep": th * PREP_BYTES_PER_TOKEN_HEAD,
+           "kda_prefill_scan": th * SCAN_BYTES_PER_TOKEN_HEAD + ck_bytes}
+    dom = max(alg, key=lambda n: kt[n]["avg_ms"])
+    dom_s = kt[dom]["avg_ms"] / 1e3
+    achieved = alg[dom] / dom_s / 1e9
+    call_bytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + ck_bytes
+    call_flops = th * PREFILL_FLOPS_PER_TOKEN_HEAD
+    step_s = dev_s / args.steps
+    out = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "d": w.D, "T": w.T, "chunk": 64,
+                   "checkpoints": list(w.ckpts), "page_bytes": w.page_bytes,
+                   "state_dtype": "f32", "io_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg[dom],
+                     "avg_launch_ms": 1e3 * dom_s},
+        "prefill_step": {"algorithmic_bytes": call_bytes, "algorithmic_flops": call_flops,
+                         "frac_hbm": call_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                         "frac_mfma_bf16": call_flops / step_s / 1e12 / BF16_PEAK_TFLOPS,
+                         "wall_s": wall_s},
+        "kernels": kt,
+    }
+    if not args.only_prefill:
+        log("decode: 256 requests x 32 heads")
+        out["decode"] = bench_decode(K, G, steps=200, warmup=10)
+        log(f"decode: {out['decode']}")
+        out["checkpoint_copy"] = bench_copy(K, steps=20, warmup=3)
+        log(f"copy: {out['checkpoint_copy']}")
+    if not args.no_cpu:
+        log("cpu baseline: oracle")
+        out["cpu_baseline"] = cpu_baseline(G, w, d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

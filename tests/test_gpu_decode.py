@@ -28,6 +28,7 @@ def _run_decode(n, H, D, steps, dtype, seed, pool_pages, page_table, sample, che
     pout = pin if in_place else torch.from_numpy(
         (page_table + pool_pages // 2).astype(np.int32)).cuda()
     # all steps' inputs: one logical [steps * n, H, D] token stream
+    print(f"decode: n={n} H={H} D={D} steps={steps}: generating inputs", flush=True)
     d = G.kda_tokens(seed, H, D, 0, steps * n, dtype)
     di = {k: dev(v, dtype) for k, v in d.items()}
     o_all = torch.empty((steps, n, H, D), dtype=tdtype(dtype), device="cuda")
