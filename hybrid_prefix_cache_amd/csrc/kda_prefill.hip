@@ -22,6 +22,8 @@
 // slab of S in fp32 registers.  Column j of S depends only on column j of v,
 // which is what allows the d_v split.  A partial final chunk is padded with
 // zero rows (k = q = v = g = beta = 0), which leave the state unchanged.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -351,6 +353,365 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// prep for bf16 inputs: two (chunk, head) pairs per 512-thread workgroup
+// ---------------------------------------------------------------------------
+// Each half of the workgroup (4 waves) owns one pair and an LDS region of at
+// most 80 KB whose parts are reused phase by phase:
+//   RA : Kt | Kh (decayed keys)  ->  L | Tinv (fp32 solve)  ->  T | T^T (bf16)
+//   RQ : Qt (decayed queries)
+//   RT : prefix partials  ->  Kt^T (keys, token-contiguous)  ->  Keff^T
+//   RAQ: Aq (masked Qt Kh^T)
+// so two pairs share a CU and their phases interleave on the SIMDs.
+// Element-wise work maps thread -> (channel pair, run of tokens), giving
+// 256-byte coalesced loads and a register prefix sum; products are formed
+// transposed (M = channels) so results reach global memory as 8-byte runs.
+template <int D> struct Prep2Layout {
+  static constexpr int NP = D / 2;             // channel pairs
+  static constexpr int TPARTS = 256 / NP;      // token runs
+  static constexpr int TPP = 64 / TPARTS;      // tokens per run
+  static constexpr int LDK = D + 8;            // [64][D] bf16 tiles
+  static constexpr int LDC = 64 + 8;           // [*][64] bf16 tiles
+  static constexpr int LDF = 65;               // fp32 [64][65]
+  static constexpr int kTileK = 64 * LDK * 2;
+  static constexpr int kRA = 0;
+  static constexpr int kRABytes = (2 * kTileK > 2 * 64 * LDF * 4) ? 2 * kTileK : 2 * 64 * LDF * 4;
+  static constexpr int kRQ = kRA + kRABytes;
+  static constexpr int kRT = kRQ + kTileK;
+  static constexpr int kRTBytes = (D * LDC * 2 > TPARTS * D * 4) ? D * LDC * 2 : TPARTS * D * 4;
+  static constexpr int kRAQ = kRT + kRTBytes;
+  static constexpr int kHalf = kRAQ + 64 * LDC * 2;
+  static_assert(kHalf <= 80 * 1024, "two pairs must fit in one CU's LDS");
+  static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kRAQ % 16 == 0 && kHalf % 16 == 0, "align");
+};
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs) {
+  using LY = Prep2Layout<D>;
+  using IO = InterOff<D>;
+  constexpr int NP = LY::NP, TPP = LY::TPP, LDK = LY::LDK, LDC = LY::LDC, LDF = LY::LDF;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int half = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int lane = t & 63, wv = t >> 6;
+  uint8_t* base = smem + half * LY::kHalf;
+  uint16_t* Kt = reinterpret_cast<uint16_t*>(base + LY::kRA);
+  uint16_t* Kh = Kt + 64 * LDK;
+  float* Lm = reinterpret_cast<float*>(base + LY::kRA);
+  float* Ti = Lm + 64 * LDF;
+  uint16_t* Tb = reinterpret_cast<uint16_t*>(base + LY::kRA);
+  uint16_t* TbT = Tb + 64 * LDC;
+  uint16_t* Qt = reinterpret_cast<uint16_t*>(base + LY::kRQ);
+  float* partial = reinterpret_cast<float*>(base + LY::kRT);
+  uint16_t* KtT = reinterpret_cast<uint16_t*>(base + LY::kRT);
+  uint16_t* KeffT = KtT;
+  uint16_t* Aq = reinterpret_cast<uint16_t*>(base + LY::kRAQ);
+
+  const int pair = 2 * blockIdx.x + half;
+  const bool active = pair < total_pairs;  // an idle half still joins every barrier
+  const int H = a.H;
+  const int chunk = active ? pair / H : 0, h = active ? pair % H : 0;
+  int len = 0;
+  int64_t row0 = 0;
+  if (active) {
+    const SeqEntry se = a.seqs[find_seq(a.seqs, a.num_seqs, chunk)];
+    const int lc = chunk - se.chunk_begin;
+    row0 = se.row_begin + 64LL * lc;
+    len = min(64, se.len - 64 * lc);
+  }
+  const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* gk = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* gg = reinterpret_cast<const uint16_t*>(a.g);
+  const uint16_t* gb = reinterpret_cast<const uint16_t*>(a.beta);
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.inter + ((int64_t)chunk * H + h) * a.blk_bytes);
+
+  // ---- A: loads (thread -> channel pair cp, token run tp) -------------------
+  const int cp = t % NP, tp = t / NP, c0 = 2 * cp, r0 = tp * TPP;
+  uint32_t gk2[TPP], gq2[TPP], gg2[TPP];
+#pragma unroll
+  for (int i = 0; i < TPP; ++i) {
+    const int r = r0 + i;
+    const bool ok = active && r < len;
+    const int64_t off = ((row0 + (ok ? r : 0)) * H + h) * D + c0;
+    gk2[i] = ok ? *reinterpret_cast<const uint32_t*>(gk + off) : 0u;
+    gq2[i] = ok ? *reinterpret_cast<const uint32_t*>(gq + off) : 0u;
+    gg2[i] = ok ? *reinterpret_cast<const uint32_t*>(gg + off) : 0u;
+  }
+
+  // ---- B: inclusive prefix sum of g over tokens (registers + run totals) ----
+  float G0[TPP], G1[TPP];
+  {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+      s0 += bf16_to_f32((uint16_t)(gg2[i] & 0xffffu));
+      s1 += bf16_to_f32((uint16_t)(gg2[i] >> 16));
+      G0[i] = s0;
+      G1[i] = s1;
+    }
+    partial[tp * D + c0] = s0;
+    partial[tp * D + c0 + 1] = s1;
+  }
+  __syncthreads();
+  float gc0 = 0.f, gc1 = 0.f, off0 = 0.f, off1 = 0.f;
+#pragma unroll
+  for (int p = 0; p < LY::TPARTS; ++p) {
+    const float v0 = partial[p * D + c0], v1 = partial[p * D + c0 + 1];
+    if (p < tp) { off0 += v0; off1 += v1; }
+    gc0 += v0;
+    gc1 += v1;
+  }
+  __syncthreads();  // partials are overwritten by Kt^T below
+
+  // ---- C: decayed tiles --------------------------------------------------------
+  {
+    const float eC0 = __expf(gc0), eC1 = __expf(gc1);
+    uint32_t ktT0[TPP / 2], ktT1[TPP / 2], ke0[TPP / 2], ke1[TPP / 2];
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+      const int r = r0 + i;
+      const float Ga = G0[i] + off0, Gb = G1[i] + off1;
+      const float e0 = __expf(Ga), e1 = __expf(Gb);
+      const float i0 = __expf(-Ga), i1 = __expf(-Gb);
+      const float k0 = bf16_to_f32((uint16_t)(gk2[i] & 0xffffu)), k1 = bf16_to_f32((uint16_t)(gk2[i] >> 16));
+      const float q0 = bf16_to_f32((uint16_t)(gq2[i] & 0xffffu)), q1 = bf16_to_f32((uint16_t)(gq2[i] >> 16));
+      const uint32_t kt = pack2(k0 * e0, k1 * e1);
+      *reinterpret_cast<uint32_t*>(Kt + r * LDK + c0) = kt;
+      *reinterpret_cast<uint32_t*>(Kh + r * LDK + c0) = pack2(k0 * i0, k1 * i1);
+      *reinterpret_cast<uint32_t*>(Qt + r * LDK + c0) = pack2(q0 * e0, q1 * e1);
+      const uint32_t ke = pack2(k0 * (eC0 * i0), k1 * (eC1 * i1));
+      if (i & 1) {
+        ktT0[i / 2] |= (kt & 0xffffu) << 16;
+        ktT1[i / 2] |= kt & 0xffff0000u;
+        ke0[i / 2] |= (ke & 0xffffu) << 16;
+        ke1[i / 2] |= ke & 0xffff0000u;
+      } else {
+        ktT0[i / 2] = kt & 0xffffu;
+        ktT1[i / 2] = kt >> 16;
+        ke0[i / 2] = ke & 0xffffu;
+        ke1[i / 2] = ke >> 16;
+      }
+    }
+    // token-contiguous runs: Kt^T rows c0, c0+1 in LDS; Kend^T rows in global
+#pragma unroll
+    for (int v = 0; v < TPP / 8; ++v) {
+      const u32x4_t a0 = {ktT0[4 * v], ktT0[4 * v + 1], ktT0[4 * v + 2], ktT0[4 * v + 3]};
+      const u32x4_t a1 = {ktT1[4 * v], ktT1[4 * v + 1], ktT1[4 * v + 2], ktT1[4 * v + 3]};
+      *reinterpret_cast<u32x4_t*>(KtT + c0 * LDC + r0 + 8 * v) = a0;
+      *reinterpret_cast<u32x4_t*>(KtT + (c0 + 1) * LDC + r0 + 8 * v) = a1;
+      if (active) {
+        const u32x4_t b0 = {ke0[4 * v], ke0[4 * v + 1], ke0[4 * v + 2], ke0[4 * v + 3]};
+        const u32x4_t b1 = {ke1[4 * v], ke1[4 * v + 1], ke1[4 * v + 2], ke1[4 * v + 3]};
+        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + c0 * 64 + r0 + 8 * v) = b0;
+        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + (c0 + 1) * 64 + r0 + 8 * v) = b1;
+      }
+    }
+    if (active && tp == 0) {
+      float* gamma = reinterpret_cast<float*>(out + IO::kGammaElems);
+      gamma[c0] = eC0;
+      gamma[c0 + 1] = eC1;
+    }
+  }
+  __syncthreads();
+
+  // ---- D: Gram matrices (waves 0,1: Kt Kh^T; waves 2,3: Qt Kh^T) --------------
+  {
+    const int gram = wv >> 1;
+    const uint16_t* Aop = gram == 0 ? Kt : Qt;
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int mt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[pass][nt] = zero4();
+        if (nt <= mt) tile_mma<uint16_t>(acc[pass][nt], Aop, LDK, 16 * mt, Kh, LDK, 16 * nt, 0, D, lane);
+      }
+    }
+    __syncthreads();  // Kt/Kh are overwritten by L below
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int mt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
+      float br[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * mt + acc_row(lane, r);
+        br[r] = (active && i < len) ? bf16_to_f32(gb[(row0 + i) * H + h]) : 0.f;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
+          if (gram == 0) {
+            if (nt <= mt) Lm[i * LDF + j] = (j < i) ? br[r] * acc[pass][nt][r] : 0.f;
+          } else {
+            Aq[i * LDC + j] = f32_to_bf16((j <= i) ? acc[pass][nt][r] : 0.f);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- E: T = (I + L)^-1 diag(beta) by 16x16 blocks ----------------------------
+  if (lane < 16) {
+    const int j = lane, b0 = 16 * wv;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc -= Lm[(b0 + i) * LDF + b0 + m] * x[m];
+      x[i] = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ti[(b0 + i) * LDF + b0 + j] = x[i];
+  }
+  __syncthreads();
+  for (int ar = 1; ar < 4; ++ar) {
+    // Y_b = sum_{c=b}^{ar-1} L_{ar,c} X_{c,b}, staged in the destination block
+    float y[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int it = t + 256 * q;
+      y[q] = 0.f;
+      if (it < ar * 256) {
+        const int b = it >> 8, i = (it >> 4) & 15, j = it & 15;
+        float acc = 0.f;
+        for (int c = b; c < ar; ++c)
+#pragma unroll
+          for (int m = 0; m < 16; ++m)
+            acc += Lm[(16 * ar + i) * LDF + 16 * c + m] * Ti[(16 * c + m) * LDF + 16 * b + j];
+        y[q] = acc;
+        Ti[(16 * ar + i) * LDF + 16 * b + j] = acc;
+      }
+    }
+    __syncthreads();
+    float x[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int it = t + 256 * q;
+      x[q] = 0.f;
+      if (it < ar * 256) {
+        const int b = it >> 8, i = (it >> 4) & 15, j = it & 15;
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          acc += Ti[(16 * ar + i) * LDF + 16 * ar + m] * Ti[(16 * ar + m) * LDF + 16 * b + j];
+        x[q] = -acc;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int it = t + 256 * q;
+      if (it < ar * 256) {
+        const int b = it >> 8, i = (it >> 4) & 15, j = it & 15;
+        Ti[(16 * ar + i) * LDF + 16 * b + j] = x[q];
+      }
+    }
+    (void)y;
+    __syncthreads();
+  }
+  {
+    // T[i][j] = Tinv[i][j] beta_j (j <= i); thread t owns column j = t & 63,
+    // rows i = (t >> 6) + 4 q
+    const int j = t & 63;
+    const float bj = (active && j < len) ? bf16_to_f32(gb[(row0 + j) * H + h]) : 0.f;
+    float tv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = (t >> 6) + 4 * q;
+      tv[q] = (j <= i) ? Ti[i * LDF + j] * bj : 0.f;
+    }
+    __syncthreads();  // Tinv is overwritten by T / T^T below
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = (t >> 6) + 4 * q;
+      const uint16_t v = f32_to_bf16(tv[q]);
+      Tb[i * LDC + j] = v;
+      TbT[j * LDC + i] = v;
+      if (active) out[IO::kT + i * 64 + j] = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- F: Keff^T = Kt^T T^T  (M = channels, N = tokens; T lower triangular) ---
+  constexpr int MTW = D / 64;  // channel tiles per wave
+  f32x4 kacc[MTW][4];
+#pragma unroll
+  for (int u = 0; u < MTW; ++u) {
+    const int mt = MTW * wv + u;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      kacc[u][nt] = zero4();
+      const int ke = nt < 2 ? 32 : 64;
+      tile_mma<uint16_t>(kacc[u][nt], KtT, LDC, 16 * mt, Tb, LDC, 16 * nt, 0, ke, lane);
+      if (active) {  // Keff[tok][ch .. ch+3]: lane holds 4 consecutive channels of one token
+        const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
+        u16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(kacc[u][nt][r]);
+        *reinterpret_cast<u16x4*>(out + IO::kKeff + tok * D + ch) = w;
+      }
+    }
+  }
+  __syncthreads();  // Kt^T is overwritten by Keff^T below
+#pragma unroll
+  for (int u = 0; u < MTW; ++u) {
+    const int mt = MTW * wv + u;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        KeffT[(16 * mt + acc_row(lane, r)) * LDC + 16 * nt + acc_col(lane)] = f32_to_bf16(kacc[u][nt][r]);
+  }
+  __syncthreads();
+
+  // ---- G: Qeff^T = Qt^T - Keff^T Aq^T ; P^T = T^T Aq^T ------------------------
+#pragma unroll
+  for (int u = 0; u < MTW; ++u) {
+    const int mt = MTW * wv + u;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 acc = zero4();
+      const int ke = nt < 2 ? 32 : 64;
+      tile_mma<uint16_t>(acc, KeffT, LDC, 16 * mt, Aq, LDC, 16 * nt, 0, ke, lane);
+      if (active) {
+        const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
+        const u16x4 qv = *reinterpret_cast<const u16x4*>(Qt + tok * LDK + ch);
+        u16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(bf16_to_f32(qv[r]) - acc[r]);
+        *reinterpret_cast<u16x4*>(out + IO::kQeff + tok * D + ch) = w;
+      }
+    }
+  }
+  {
+    // P^T tiles (mt = column block of P, nt = row block): wave wv computes nt = wv
+    const int nt = wv;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 acc = zero4();
+      if (mt <= nt) {
+        const int kb = (16 * mt) / 32 * 32, ke = nt < 2 ? 32 : 64;
+        tile_mma<uint16_t>(acc, TbT, LDC, 16 * mt, Aq, LDC, 16 * nt, kb, ke, lane);
+      }
+      if (active) {
+        const int tok = 16 * nt + acc_col(lane), col = 16 * mt + acc_row(lane, 0);
+        u16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(acc[r]);
+        *reinterpret_cast<u16x4*>(out + IO::kP + tok * 64 + col) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // scan: the state-dependent chain, chunk after chunk
 // ---------------------------------------------------------------------------
 
@@ -383,11 +744,65 @@ __device__ __forceinline__ void s_store(const f32x4* S, float* dst, int srow0, i
       dst[(srow0 + 16 * t + acc_row(lane, r)) * D + c0 + acc_col(lane)] = S[t][r];
 }
 
+// Register-resident operands of one chunk for one wave: A fragments of its
+// rows of Keff, Qeff, T, P (W/O rows 16w..16w+15) and of KendT (S rows owned by
+// the wave), the wave's decay factors gamma_C, and this thread's 4 V values.
+template <int D, typename Op> struct ChunkFrags {
+  static constexpr int KK = OpT<Op>::kK, NKD = D / KK, NKC = 64 / KK, MT = D / 64;
+  Frag<Op> keff[NKD], qeff[NKD], t[NKC], p[NKC], kend[MT][NKC];
+  f32x4 gam[MT];
+  // this thread's 4 V values, kept in the input encoding until used so that
+  // no conversion forces a wait on the prefetch
+  typename std::conditional<sizeof(Op) == 2, u16x4, f32x4>::type vraw;
+};
+
+struct ScanCtx {
+  const uint8_t* inter;
+  int64_t blk_bytes;
+  const void* v;
+  int H, h, c0, srow0, wave, lane, vt, vq;
+  int64_t row_begin;
+  int len, chunk_begin;
+};
+
+// Issue every global load chunk n needs (no waits here: the compiler's
+// counters make the consumer wait only when it touches these registers).
+template <int D, typename Op>
+__device__ __forceinline__ void load_chunk(ChunkFrags<D, Op>& f, const ScanCtx& c, int n) {
+  using CF = ChunkFrags<D, Op>;
+  using IO = InterOff<D>;
+  const Op* blk = reinterpret_cast<const Op*>(
+      c.inter + ((int64_t)(c.chunk_begin + n) * c.H + c.h) * c.blk_bytes);
+#pragma unroll
+  for (int i = 0; i < CF::NKD; ++i) {
+    f.keff[i] = frag<Op>(blk + IO::kKeff, D, 16 * c.wave, i * CF::KK, c.lane);
+    f.qeff[i] = frag<Op>(blk + IO::kQeff, D, 16 * c.wave, i * CF::KK, c.lane);
+  }
+#pragma unroll
+  for (int i = 0; i < CF::NKC; ++i) {
+    f.t[i] = frag<Op>(blk + IO::kT, 64, 16 * c.wave, i * CF::KK, c.lane);
+    f.p[i] = frag<Op>(blk + IO::kP, 64, 16 * c.wave, i * CF::KK, c.lane);
+  }
+#pragma unroll
+  for (int t = 0; t < CF::MT; ++t) {
+#pragma unroll
+    for (int i = 0; i < CF::NKC; ++i)
+      f.kend[t][i] = frag<Op>(blk + IO::kKendT, 64, c.srow0 + 16 * t, i * CF::KK, c.lane);
+    const float* gam = reinterpret_cast<const float*>(blk + IO::kGammaElems);
+    f.gam[t] = *reinterpret_cast<const f32x4*>(gam + c.srow0 + 16 * t + 4 * (c.lane >> 4));
+  }
+  const int len = min(64, c.len - 64 * n);
+  using VR = decltype(f.vraw);
+  const Op* vp = reinterpret_cast<const Op*>(c.v) +
+                 ((c.row_begin + 64LL * n + min(c.vt, len - 1)) * c.H + c.h) * D + c.c0 + c.vq;
+  f.vraw = *reinterpret_cast<const VR*>(vp);  // rows past the chunk end are zeroed at use
+}
+
 template <int D, typename Op>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   using OT = OpT<Op>;
-  using IO = InterOff<D>;
-  constexpr int NS = D / kBV, MT = D / 64;
+  constexpr int NS = D / kBV, MT = D / 64, KK = OT::kK;
+  constexpr int PF = sizeof(Op) == 2 ? 2 : 1;  // chunks of operands prefetched ahead
   constexpr int PAD = 16 / (int)sizeof(Op);
   constexpr int LDS_ = D + PAD, LDW = 64 + PAD, LDO = kBV + 1;
   __shared__ __align__(16) Op Sb[kBV * LDS_];  // S^T slab [col][row], MFMA B operand
@@ -402,10 +817,29 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int H = a.H, h = p % H;
   const SeqEntry se = a.seqs[a.order[p / H]];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c0 = slab * kBV;
-  const int srow0 = wave * (D / 4);
+  ScanCtx c;
+  c.inter = a.inter;
+  c.blk_bytes = a.blk_bytes;
+  c.v = a.v;
+  c.H = H;
+  c.h = h;
+  c.c0 = slab * kBV;
+  c.srow0 = wave * (D / 4);
+  c.wave = wave;
+  c.lane = lane;
+  c.vt = tid >> 2;        // V / O tile: token
+  c.vq = (tid & 3) * 4;   // 4-column quad
+  c.row_begin = se.row_begin;
+  c.len = se.len;
+  c.chunk_begin = se.chunk_begin;
   const int64_t hoff = (int64_t)h * D * D;
-  const Op* gv = reinterpret_cast<const Op*>(a.v);
+  const int nchunks = (se.len + 63) / 64;
+
+  ChunkFrags<D, Op> f0, f1, f2;
+  if (nchunks > 0) {
+    load_chunk<D, Op>(f0, c, 0);
+    if (PF == 2) load_chunk<D, Op>(f1, c, min(1, nchunks - 1));
+  }
 
   f32x4 S[MT];
   if (se.state_in >= 0) {
@@ -414,77 +848,102 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S[t][r] = src[(srow0 + 16 * t + acc_row(lane, r)) * D + c0 + acc_col(lane)];
+        S[t][r] = src[(c.srow0 + 16 * t + acc_row(lane, r)) * D + c.c0 + acc_col(lane)];
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t) S[t] = zero4();
   }
-  s_to_lds<D, Op>(S, Sb, LDS_, srow0, lane);
+  s_to_lds<D, Op>(S, Sb, LDS_, c.srow0, lane);
 
   int nck = se.ckpt_begin;
-  const int nchunks = (se.len + 63) / 64;
-  const int vt = tid >> 2, vq = (tid & 3) * 4;  // V / O tile: token, 4-column quad
-  for (int n = 0; n < nchunks; ++n) {
-    const int64_t row0 = se.row_begin + 64LL * n;
-    const int len = min(64, se.len - 64 * n);
-    const Op* blkp = reinterpret_cast<const Op*>(
-        a.inter + ((int64_t)(se.chunk_begin + n) * H + h) * a.blk_bytes);
+  int64_t next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
 
-    {  // V slab -> Vb (transposed)
-      float x[4] = {0.f, 0.f, 0.f, 0.f};
-      if (vt < len) load4(gv + ((row0 + vt) * H + h) * D + c0 + vq, x);
+  // One chunk: compute with `cur`, prefetch chunk n + PF into `pre`.  The
+  // prefetch is unconditional (clamped to the last chunk; a re-read at the
+  // tail is harmless) so the load counters stay exact in straight-line code.
+  auto step = [&](ChunkFrags<D, Op>& cur, ChunkFrags<D, Op>& pre, int n) {
+    load_chunk<D, Op>(pre, c, min(n + PF, nchunks - 1));
+    {
+      const bool live = c.vt < min(64, se.len - 64 * n);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Vb[(vq + j) * LDW + vt] = OT::from_f(x[j]);
+      for (int j = 0; j < 4; ++j)
+        Vb[(c.vq + j) * LDW + c.vt] = live ? cur.vraw[j] : Op(0);
     }
-    __syncthreads();
+    __syncthreads();  // Vb and Sb ready
 
-    // rows 16*wave .. +15 of W and O
     f32x4 U = zero4(), O = zero4(), X = zero4();
-    tile_mma<Op>(U, blkp + IO::kT, 64, 16 * wave, Vb, LDW, 0, 0, 64, lane);
-    tile_mma<Op>(O, blkp + IO::kP, 64, 16 * wave, Vb, LDW, 0, 0, 64, lane);
-    tile_mma<Op>(X, blkp + IO::kKeff, D, 16 * wave, Sb, LDS_, 0, 0, D, lane);
-    tile_mma<Op>(O, blkp + IO::kQeff, D, 16 * wave, Sb, LDS_, 0, 0, D, lane);
+#pragma unroll
+    for (int i = 0; i < 64 / KK; ++i) {
+      const Frag<Op> b = frag<Op>(Vb, LDW, 0, i * KK, lane);
+      mfma(U, cur.t[i], b);
+      mfma(O, cur.p[i], b);
+    }
+#pragma unroll
+    for (int i = 0; i < D / KK; ++i) {
+      const Frag<Op> b = frag<Op>(Sb, LDS_, 0, i * KK, lane);
+      mfma(X, cur.keff[i], b);
+      mfma(O, cur.qeff[i], b);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = 16 * wave + acc_row(lane, r), col = acc_col(lane);
       Wb[col * LDW + tok] = OT::from_f(U[r] - X[r]);
       Ob[tok * LDO + col] = O[r];
     }
-    __syncthreads();
+    __syncthreads();  // Wb and Ob ready; every wave is done reading Sb and Vb
 
     // S <- diag(gamma_C) S + Kend^T W
-    const float* gam = reinterpret_cast<const float*>(blkp + IO::kGammaElems);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[t][r] *= gam[srow0 + 16 * t + acc_row(lane, r)];
-      tile_mma<Op>(S[t], blkp + IO::kKendT, 64, srow0 + 16 * t, Wb, LDW, 0, 0, 64, lane);
+      for (int r = 0; r < 4; ++r) S[t][r] *= cur.gam[t][r];
+#pragma unroll
+      for (int i = 0; i < 64 / KK; ++i) mfma(S[t], cur.kend[t][i], frag<Op>(Wb, LDW, 0, i * KK, lane));
     }
-    const int64_t pend = se.start_pos + 64LL * n + len;
-    if (nck < se.ckpt_end && a.ckpts[nck].pos == pend) {
+    const int len = min(64, se.len - 64 * n);
+    if (se.start_pos + 64LL * n + len == next_pos) {
       float* dst = reinterpret_cast<float*>(a.pool + a.ckpts[nck].page * a.page_bytes) + hoff;
-      s_store<D>(S, dst, srow0, c0, lane);
+      s_store<D>(S, dst, c.srow0, c.c0, lane);
       ++nck;
+      next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
     }
-    s_to_lds<D, Op>(S, Sb, LDS_, srow0, lane);
+    s_to_lds<D, Op>(S, Sb, LDS_, c.srow0, lane);
 
-    if (vt < len) {  // output rows
-      const int64_t base = ((row0 + vt) * H + h) * D + c0 + vq;
+    if (c.vt < len) {  // output rows
+      const int64_t base = ((c.row_begin + 64LL * n + c.vt) * H + h) * D + c.c0 + c.vq;
       if (a.out_bf16) {
         u16x4 w;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16(Ob[vt * LDO + vq + j]);
+        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16(Ob[c.vt * LDO + c.vq + j]);
         *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + base) = w;
       } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + base) =
-            float4{Ob[vt * LDO + vq], Ob[vt * LDO + vq + 1], Ob[vt * LDO + vq + 2],
-                   Ob[vt * LDO + vq + 3]};
+            float4{Ob[c.vt * LDO + c.vq], Ob[c.vt * LDO + c.vq + 1], Ob[c.vt * LDO + c.vq + 2],
+                   Ob[c.vt * LDO + c.vq + 3]};
       }
     }
+  };
+
+  int n = 0;
+  if constexpr (PF == 2) {
+    for (; n + 3 <= nchunks; n += 3) {
+      step(f0, f2, n);
+      step(f1, f0, n + 1);
+      step(f2, f1, n + 2);
+    }
+    if (n < nchunks) step(f0, f2, n);
+    if (n + 1 < nchunks) step(f1, f0, n + 1);
+  } else {
+    for (; n + 2 <= nchunks; n += 2) {
+      step(f0, f1, n);
+      step(f1, f0, n + 1);
+    }
+    if (n < nchunks) step(f0, f1, n);
   }
+  (void)f2;
   if (se.state_out >= 0) {
     float* dst = reinterpret_cast<float*>(a.pool + se.state_out * a.page_bytes) + hoff;
-    s_store<D>(S, dst, srow0, c0, lane);
+    s_store<D>(S, dst, c.srow0, c.c0, lane);
   }
 }
 
@@ -513,11 +972,19 @@ static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_prep2_t(const PrepArgs& a, int total_chunks, hipStream_t st) {
+  constexpr int kBytes = 2 * Prep2Layout<D>::kHalf;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prep2_kernel<D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
+  const int pairs = total_chunks * a.H;
+  hipLaunchKernelGGL((prep2_kernel<D>), dim3((pairs + 1) / 2), dim3(512), kBytes, st, a, pairs);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep(int D, bool bf16, const PrepArgs& a, int total_chunks, hipStream_t st) {
-  if (D == 128) return bf16 ? launch_prep_t<128, uint16_t>(a, total_chunks, st)
-                            : launch_prep_t<128, float>(a, total_chunks, st);
-  return bf16 ? launch_prep_t<64, uint16_t>(a, total_chunks, st)
-              : launch_prep_t<64, float>(a, total_chunks, st);
+  if (bf16) return D == 128 ? launch_prep2_t<128>(a, total_chunks, st) : launch_prep2_t<64>(a, total_chunks, st);
+  return D == 128 ? launch_prep_t<128, float>(a, total_chunks, st) : launch_prep_t<64, float>(a, total_chunks, st);
 }
 
 hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st) {
