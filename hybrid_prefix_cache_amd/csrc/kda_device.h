@@ -23,6 +23,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kChunk = 64;     // tokens per chunk (C)
 constexpr int kThreads = 256;  // 4 waves per workgroup
@@ -32,12 +33,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
+// fp32 -> bf16, round to nearest even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32), two values per instruction when paired.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+// two / four values packed in one conversion each pair
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---- storage-type traits --------------------------------------------------
@@ -120,6 +126,12 @@ __device__ __forceinline__ void tile_mma_kn(f32x4& acc, const float* A, int lda,
     Frag<float> b = frag_kn(B, ldb, n0, k, lane);
     mfma(acc, a, b);
   }
+}
+
+__device__ __forceinline__ u16x4 pack_bf16x4(float a, float b, float c, float d) {
+  bf16x4_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c),
+                static_cast<__bf16>(d)};
+  return __builtin_bit_cast(u16x4, v);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }

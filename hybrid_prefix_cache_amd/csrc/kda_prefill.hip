@@ -384,9 +384,7 @@ template <int D> struct Prep2Layout {
   static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kRAQ % 16 == 0 && kHalf % 16 == 0, "align");
 };
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
 
 template <int D>
 __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs) {
@@ -725,90 +723,71 @@ template <int D> struct ScanGrid {
   __host__ __device__ static int grid(int npairs) { return 8 * NS * ((npairs + 7) / 8); }
 };
 
-template <int D, typename Op>
-__device__ __forceinline__ void s_to_lds(const f32x4* S, Op* Sb, int ldS, int srow0, int lane) {
-  using OT = OpT<Op>;
-#pragma unroll
-  for (int t = 0; t < D / 64; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Sb[acc_col(lane) * ldS + srow0 + 16 * t + acc_row(lane, r)] = OT::from_f(S[t][r]);
-}
-
-template <int D>
-__device__ __forceinline__ void s_store(const f32x4* S, float* dst, int srow0, int c0, int lane) {
-#pragma unroll
-  for (int t = 0; t < D / 64; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      dst[(srow0 + 16 * t + acc_row(lane, r)) * D + c0 + acc_col(lane)] = S[t][r];
-}
-
-// Register-resident operands of one chunk for one wave: A fragments of its
-// rows of Keff, Qeff, T, P (W/O rows 16w..16w+15) and of KendT (S rows owned by
-// the wave), the wave's decay factors gamma_C, and this thread's 4 V values.
-template <int D, typename Op> struct ChunkFrags {
-  static constexpr int KK = OpT<Op>::kK, NKD = D / KK, NKC = 64 / KK, MT = D / 64;
-  Frag<Op> keff[NKD], qeff[NKD], t[NKC], p[NKC], kend[MT][NKC];
-  f32x4 gam[MT];
-  // this thread's 4 V values, kept in the input encoding until used so that
-  // no conversion forces a wait on the prefetch
-  typename std::conditional<sizeof(Op) == 2, u16x4, f32x4>::type vraw;
+// Scan workgroup: 8 waves on one (sequence, head, 16-column slab).
+//   waves 0-3 ("W"): rows 16w..16w+15 of W = T V - Keff S          -> LDS
+//   waves 4-7 ("O"): the same rows of O, formed transposed,
+//                    O^T = V^T P^T + S^T Qeff^T, stored as 4-column runs
+//   every wave that owns an S tile (rows 16w..16w+15) applies
+//                    S <- diag(gamma_C) S + Kend^T W.
+// Operands of chunk n+PF are loaded into registers while chunk n computes.
+template <int D, typename Op> struct ChunkOps {
+  static constexpr int KK = OpT<Op>::kK, NKD = D / KK, NKC = 64 / KK;
+  Frag<Op> fa[NKC];  // W waves: T rows; O waves: P rows
+  Frag<Op> fb[NKD];  // W waves: Keff rows; O waves: Qeff rows
+  Frag<Op> fe[NKC];  // Kend^T rows of the wave's S tile
+  f32x4 gam;         // gamma_C of the 4 S rows this lane holds
+  typename std::conditional<sizeof(Op) == 2, uint32_t, u32x2_t>::type vraw;  // 2 V values
 };
 
 struct ScanCtx {
   const uint8_t* inter;
   int64_t blk_bytes;
   const void* v;
-  int H, h, c0, srow0, wave, lane, vt, vq;
+  int H, h, c0, wv, lane, vt, vc;
+  bool is_o, owns_s;
   int64_t row_begin;
   int len, chunk_begin;
 };
 
-// Issue every global load chunk n needs (no waits here: the compiler's
-// counters make the consumer wait only when it touches these registers).
 template <int D, typename Op>
-__device__ __forceinline__ void load_chunk(ChunkFrags<D, Op>& f, const ScanCtx& c, int n) {
-  using CF = ChunkFrags<D, Op>;
+__device__ __forceinline__ void load_ops(ChunkOps<D, Op>& f, const ScanCtx& c, int n) {
+  using CO = ChunkOps<D, Op>;
   using IO = InterOff<D>;
   const Op* blk = reinterpret_cast<const Op*>(
       c.inter + ((int64_t)(c.chunk_begin + n) * c.H + c.h) * c.blk_bytes);
+  const int rt = c.wv & 3;
+  const Op* pa = blk + (c.is_o ? IO::kP : IO::kT);
+  const Op* pb = blk + (c.is_o ? IO::kQeff : IO::kKeff);
 #pragma unroll
-  for (int i = 0; i < CF::NKD; ++i) {
-    f.keff[i] = frag<Op>(blk + IO::kKeff, D, 16 * c.wave, i * CF::KK, c.lane);
-    f.qeff[i] = frag<Op>(blk + IO::kQeff, D, 16 * c.wave, i * CF::KK, c.lane);
-  }
+  for (int i = 0; i < CO::NKC; ++i) f.fa[i] = frag<Op>(pa, 64, 16 * rt, i * CO::KK, c.lane);
 #pragma unroll
-  for (int i = 0; i < CF::NKC; ++i) {
-    f.t[i] = frag<Op>(blk + IO::kT, 64, 16 * c.wave, i * CF::KK, c.lane);
-    f.p[i] = frag<Op>(blk + IO::kP, 64, 16 * c.wave, i * CF::KK, c.lane);
-  }
+  for (int i = 0; i < CO::NKD; ++i) f.fb[i] = frag<Op>(pb, D, 16 * rt, i * CO::KK, c.lane);
+  {  // unconditional (a wave without an S tile reads a valid row it ignores)
+    const int srow = min(16 * c.wv, D - 16);
 #pragma unroll
-  for (int t = 0; t < CF::MT; ++t) {
-#pragma unroll
-    for (int i = 0; i < CF::NKC; ++i)
-      f.kend[t][i] = frag<Op>(blk + IO::kKendT, 64, c.srow0 + 16 * t, i * CF::KK, c.lane);
+    for (int i = 0; i < CO::NKC; ++i)
+      f.fe[i] = frag<Op>(blk + IO::kKendT, 64, srow, i * CO::KK, c.lane);
     const float* gam = reinterpret_cast<const float*>(blk + IO::kGammaElems);
-    f.gam[t] = *reinterpret_cast<const f32x4*>(gam + c.srow0 + 16 * t + 4 * (c.lane >> 4));
+    f.gam = *reinterpret_cast<const f32x4*>(gam + srow + 4 * (c.lane >> 4));
   }
   const int len = min(64, c.len - 64 * n);
   using VR = decltype(f.vraw);
   const Op* vp = reinterpret_cast<const Op*>(c.v) +
-                 ((c.row_begin + 64LL * n + min(c.vt, len - 1)) * c.H + c.h) * D + c.c0 + c.vq;
+                 ((c.row_begin + 64LL * n + min(c.vt, len - 1)) * c.H + c.h) * D + c.c0 + c.vc;
   f.vraw = *reinterpret_cast<const VR*>(vp);  // rows past the chunk end are zeroed at use
 }
 
 template <int D, typename Op>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   using OT = OpT<Op>;
-  constexpr int NS = D / kBV, MT = D / 64, KK = OT::kK;
-  constexpr int PF = sizeof(Op) == 2 ? 2 : 1;  // chunks of operands prefetched ahead
+  using CO = ChunkOps<D, Op>;
+  constexpr int NS = D / kBV, KK = OT::kK;
+  constexpr int PF = sizeof(Op) == 2 ? 3 : 1;  // chunks of operands prefetched ahead
   constexpr int PAD = 16 / (int)sizeof(Op);
-  constexpr int LDS_ = D + PAD, LDW = 64 + PAD, LDO = kBV + 1;
-  __shared__ __align__(16) Op Sb[kBV * LDS_];  // S^T slab [col][row], MFMA B operand
+  constexpr int LDS_ = D + PAD, LDW = 64 + PAD;
+  __shared__ __align__(16) Op Sb[kBV * LDS_];  // S^T slab [col][row]
   __shared__ __align__(16) Op Wb[kBV * LDW];   // W^T [col][token]
   __shared__ __align__(16) Op Vb[kBV * LDW];   // V^T [col][token]
-  __shared__ float Ob[64 * LDO];               // output staging [token][col]
 
   const int L = blockIdx.x;
   const int xcd = L & 7, slab = (L >> 3) % NS, blk = L / (8 * NS);
@@ -816,7 +795,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   if (p >= a.npairs) return;
   const int H = a.H, h = p % H;
   const SeqEntry se = a.seqs[a.order[p / H]];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   ScanCtx c;
   c.inter = a.inter;
   c.blk_bytes = a.blk_bytes;
@@ -824,115 +803,124 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   c.H = H;
   c.h = h;
   c.c0 = slab * kBV;
-  c.srow0 = wave * (D / 4);
-  c.wave = wave;
+  c.wv = wv;
   c.lane = lane;
-  c.vt = tid >> 2;        // V / O tile: token
-  c.vq = (tid & 3) * 4;   // 4-column quad
+  c.vt = tid >> 3;       // V tile: token
+  c.vc = (tid & 7) * 2;  // V tile: column pair
+  c.is_o = wv >= 4;
+  c.owns_s = 16 * wv < D;
   c.row_begin = se.row_begin;
   c.len = se.len;
   c.chunk_begin = se.chunk_begin;
+  const int rt = wv & 3;
   const int64_t hoff = (int64_t)h * D * D;
   const int nchunks = (se.len + 63) / 64;
 
-  ChunkFrags<D, Op> f0, f1, f2;
+  ChunkOps<D, Op> f0, f1, f2, f3;
   if (nchunks > 0) {
-    load_chunk<D, Op>(f0, c, 0);
-    if (PF == 2) load_chunk<D, Op>(f1, c, min(1, nchunks - 1));
+    load_ops<D, Op>(f0, c, 0);
+    if (PF >= 2) load_ops<D, Op>(f1, c, min(1, nchunks - 1));
+    if (PF >= 3) load_ops<D, Op>(f2, c, min(2, nchunks - 1));
   }
 
-  f32x4 S[MT];
-  if (se.state_in >= 0) {
+  // this wave's S tile: rows 16*wv + 4*(lane/16) + r, column c0 + lane%16
+  f32x4 S = zero4();
+  if (c.owns_s && se.state_in >= 0) {
     const float* src = reinterpret_cast<const float*>(a.pool + se.state_in * a.page_bytes) + hoff;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[t][r] = src[(c.srow0 + 16 * t + acc_row(lane, r)) * D + c.c0 + acc_col(lane)];
-  } else {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) S[t] = zero4();
+    for (int r = 0; r < 4; ++r) S[r] = src[(16 * wv + acc_row(lane, r)) * D + c.c0 + acc_col(lane)];
   }
-  s_to_lds<D, Op>(S, Sb, LDS_, c.srow0, lane);
+  auto s_to_lds = [&]() {
+    if (c.owns_s) {
+      if constexpr (sizeof(Op) == 2) {
+        *reinterpret_cast<u16x4*>(Sb + acc_col(lane) * LDS_ + 16 * wv + acc_row(lane, 0)) =
+            pack_bf16x4(S[0], S[1], S[2], S[3]);
+      } else {
+        *reinterpret_cast<f32x4*>(Sb + acc_col(lane) * LDS_ + 16 * wv + acc_row(lane, 0)) = S;
+      }
+    }
+  };
+  auto s_store = [&](int page) {
+    if (c.owns_s) {
+      float* dst = reinterpret_cast<float*>(a.pool + page * a.page_bytes) + hoff;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * wv + acc_row(lane, r)) * D + c.c0 + acc_col(lane)] = S[r];
+    }
+  };
+  s_to_lds();
 
   int nck = se.ckpt_begin;
   int64_t next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
 
-  // One chunk: compute with `cur`, prefetch chunk n + PF into `pre`.  The
-  // prefetch is unconditional (clamped to the last chunk; a re-read at the
-  // tail is harmless) so the load counters stay exact in straight-line code.
-  auto step = [&](ChunkFrags<D, Op>& cur, ChunkFrags<D, Op>& pre, int n) {
-    load_chunk<D, Op>(pre, c, min(n + PF, nchunks - 1));
-    {
-      const bool live = c.vt < min(64, se.len - 64 * n);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        Vb[(c.vq + j) * LDW + c.vt] = live ? cur.vraw[j] : Op(0);
+  auto step = [&](CO& cur, CO& pre, int n) {
+    load_ops<D, Op>(pre, c, min(n + PF, nchunks - 1));
+    const int len = min(64, se.len - 64 * n);
+    {  // V tile -> Vb (transposed), rows past the chunk end as zeros
+      const bool live = c.vt < len;
+      if constexpr (sizeof(Op) == 2) {
+        Vb[c.vc * LDW + c.vt] = live ? (uint16_t)(cur.vraw & 0xffffu) : (uint16_t)0;
+        Vb[(c.vc + 1) * LDW + c.vt] = live ? (uint16_t)(cur.vraw >> 16) : (uint16_t)0;
+      } else {
+        Vb[c.vc * LDW + c.vt] = live ? __uint_as_float(cur.vraw[0]) : 0.f;
+        Vb[(c.vc + 1) * LDW + c.vt] = live ? __uint_as_float(cur.vraw[1]) : 0.f;
+      }
     }
     __syncthreads();  // Vb and Sb ready
 
-    f32x4 U = zero4(), O = zero4(), X = zero4();
+    if (!c.is_o) {
+      f32x4 U = zero4(), X = zero4();
 #pragma unroll
-    for (int i = 0; i < 64 / KK; ++i) {
-      const Frag<Op> b = frag<Op>(Vb, LDW, 0, i * KK, lane);
-      mfma(U, cur.t[i], b);
-      mfma(O, cur.p[i], b);
-    }
+      for (int i = 0; i < CO::NKC; ++i) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 0, i * KK, lane));
 #pragma unroll
-    for (int i = 0; i < D / KK; ++i) {
-      const Frag<Op> b = frag<Op>(Sb, LDS_, 0, i * KK, lane);
-      mfma(X, cur.keff[i], b);
-      mfma(O, cur.qeff[i], b);
-    }
+      for (int i = 0; i < CO::NKD; ++i) mfma(X, cur.fb[i], frag<Op>(Sb, LDS_, 0, i * KK, lane));
+      Op* wdst = Wb + acc_col(lane) * LDW + 16 * rt + acc_row(lane, 0);
+      if constexpr (sizeof(Op) == 2) {
+        *reinterpret_cast<u16x4*>(wdst) = pack_bf16x4(U[0] - X[0], U[1] - X[1], U[2] - X[2], U[3] - X[3]);
+      } else {
+        *reinterpret_cast<f32x4*>(wdst) = U - X;
+      }
+    } else {
+      f32x4 OT4 = zero4();  // O^T[col = 4*(lane/16) + r][token = 16*rt + lane%16]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = 16 * wave + acc_row(lane, r), col = acc_col(lane);
-      Wb[col * LDW + tok] = OT::from_f(U[r] - X[r]);
-      Ob[tok * LDO + col] = O[r];
+      for (int i = 0; i < CO::NKC; ++i) mfma(OT4, frag<Op>(Vb, LDW, 0, i * KK, lane), cur.fa[i]);
+#pragma unroll
+      for (int i = 0; i < CO::NKD; ++i) mfma(OT4, frag<Op>(Sb, LDS_, 0, i * KK, lane), cur.fb[i]);
+      const int tok = 16 * rt + acc_col(lane);
+      if (tok < len) {
+        const int64_t base = ((c.row_begin + 64LL * n + tok) * H + h) * D + c.c0 + acc_row(lane, 0);
+        if (a.out_bf16)
+          *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + base) =
+              pack_bf16x4(OT4[0], OT4[1], OT4[2], OT4[3]);
+        else
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + base) = OT4;
+      }
     }
-    __syncthreads();  // Wb and Ob ready; every wave is done reading Sb and Vb
+    __syncthreads();  // Wb ready; every wave is done reading Sb and Vb
 
-    // S <- diag(gamma_C) S + Kend^T W
+    if (c.owns_s) {  // S <- diag(gamma_C) S + Kend^T W
+      S *= cur.gam;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[t][r] *= cur.gam[t][r];
-#pragma unroll
-      for (int i = 0; i < 64 / KK; ++i) mfma(S[t], cur.kend[t][i], frag<Op>(Wb, LDW, 0, i * KK, lane));
+      for (int i = 0; i < CO::NKC; ++i) mfma(S, cur.fe[i], frag<Op>(Wb, LDW, 0, i * KK, lane));
     }
-    const int len = min(64, se.len - 64 * n);
     if (se.start_pos + 64LL * n + len == next_pos) {
-      float* dst = reinterpret_cast<float*>(a.pool + a.ckpts[nck].page * a.page_bytes) + hoff;
-      s_store<D>(S, dst, c.srow0, c.c0, lane);
+      s_store(a.ckpts[nck].page);
       ++nck;
       next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
     }
-    s_to_lds<D, Op>(S, Sb, LDS_, c.srow0, lane);
-
-    if (c.vt < len) {  // output rows
-      const int64_t base = ((c.row_begin + 64LL * n + c.vt) * H + h) * D + c.c0 + c.vq;
-      if (a.out_bf16) {
-        u16x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = f32_to_bf16(Ob[c.vt * LDO + c.vq + j]);
-        *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + base) = w;
-      } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.o) + base) =
-            float4{Ob[c.vt * LDO + c.vq], Ob[c.vt * LDO + c.vq + 1], Ob[c.vt * LDO + c.vq + 2],
-                   Ob[c.vt * LDO + c.vq + 3]};
-      }
-    }
+    s_to_lds();
   };
 
   int n = 0;
-  if constexpr (PF == 2) {
-    for (; n + 3 <= nchunks; n += 3) {
-      step(f0, f2, n);
+  if constexpr (PF == 3) {
+    for (; n + 4 <= nchunks; n += 4) {
+      step(f0, f3, n);
       step(f1, f0, n + 1);
       step(f2, f1, n + 2);
+      step(f3, f2, n + 3);
     }
-    if (n < nchunks) step(f0, f2, n);
+    if (n < nchunks) step(f0, f3, n);
     if (n + 1 < nchunks) step(f1, f0, n + 1);
+    if (n + 2 < nchunks) step(f2, f1, n + 2);
   } else {
     for (; n + 2 <= nchunks; n += 2) {
       step(f0, f1, n);
@@ -941,10 +929,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     if (n < nchunks) step(f0, f1, n);
   }
   (void)f2;
-  if (se.state_out >= 0) {
-    float* dst = reinterpret_cast<float*>(a.pool + se.state_out * a.page_bytes) + hoff;
-    s_store<D>(S, dst, c.srow0, c.c0, lane);
-  }
+  (void)f3;
+  if (se.state_out >= 0) s_store(se.state_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -968,7 +954,7 @@ static hipError_t launch_prep_t(const PrepArgs& a, int total_chunks, hipStream_t
 
 template <int D, typename Op>
 static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((scan_kernel<D, Op>), dim3(ScanGrid<D>::grid(a.npairs)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((scan_kernel<D, Op>), dim3(ScanGrid<D>::grid(a.npairs)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
