@@ -134,6 +134,28 @@ __device__ __forceinline__ u16x4 pack_bf16x4(float a, float b, float c, float d)
   return __builtin_bit_cast(u16x4, v);
 }
 
+// Fragment-major storage of an MFMA operand X[rows][K] (the layout the
+// prefill prep kernel writes its per-chunk intermediates in): fragment
+// (row tile, k step) is 64 lanes x (KK/4) contiguous elements, lane-major, so a
+// wave loads one fragment as one contiguous 1 KB (bf16) / 256 B (fp32) block.
+template <int KK>
+__host__ __device__ __forceinline__ int frag_off(int row, int k, int K) {
+  constexpr int E = KK / 4;  // elements per lane
+  const int f = (row >> 4) * (K / KK) + k / KK;
+  const int ln = (row & 15) + 16 * ((k % KK) / E);
+  return (f * 64 + ln) * E + (k % E);
+}
+
+template <typename Op>
+__device__ __forceinline__ Frag<Op> frag_fm(const Op* x, int row_tile, int k_step, int K, int lane) {
+  constexpr int KK = OpT<Op>::kK, E = KK / 4;
+  const Op* p = x + ((row_tile * (K / KK) + k_step) * 64 + lane) * E;
+  Frag<Op> f;
+  if constexpr (E == 8) f.v = *reinterpret_cast<const u16x8*>(p);
+  else f.v = *p;
+  return f;
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Row/column of element r (0..3) of a 16x16 accumulator held by `lane`.

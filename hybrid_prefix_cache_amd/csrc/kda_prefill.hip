@@ -82,7 +82,9 @@ __device__ __forceinline__ int find_seq(const SeqEntry* seqs, int n, int chunk) 
   return lo;
 }
 
-// Offsets (in Op elements) of the pieces of one (chunk, head) block.
+// Offsets (in Op elements) of the pieces of one (chunk, head) block.  Every
+// piece is stored fragment-major (see frag_off) as the scan's MFMA operand:
+// Keff, Qeff, T, P by token rows, KendT by channel rows.
 template <int D> struct InterOff {
   static constexpr int kKeff = 0;
   static constexpr int kQeff = 64 * D;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       kt[j] = kx[j] * e;
       kh[j] = kx[j] * ei;
       qt[j] = qx[j] * e;
-      out[IO::kKendT + (c0 + j) * 64 + r] = OT::from_f(kx[j] * eci);
+      out[IO::kKendT + frag_off<KK>(c0 + j, r, 64)] = OT::from_f(kx[j] * eci);
       if constexpr (LY::kBf) KtT[(c0 + j) * LDC + r] = OT::from_f(kt[j]);
     }
     store8(Kt + r * LDK + c0, kt);
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     } else {
       Ti[i * LDF + j] = t;
     }
-    out[IO::kT + i * 64 + j] = tb;
+    out[IO::kT + frag_off<KK>(i, j, 64)] = tb;
   }
   __syncthreads();
 
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
         const Op v = OT::from_f(acc[r]);
-        out[IO::kKeff + i * D + j] = v;
+        out[IO::kKeff + frag_off<KK>(i, j, D)] = v;
         if constexpr (LY::kBf)
           KeffT[j * LDC + i] = v;
         else
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-        out[IO::kQeff + i * D + j] = OT::from_f(OT::to_f(Qt[i * LDK + j]) - acc[r]);
+        out[IO::kQeff + frag_off<KK>(i, j, D)] = OT::from_f(OT::to_f(Qt[i * LDK + j]) - acc[r]);
       }
     }
     for (int nt = 0; nt < 4; ++nt) {
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-        out[IO::kP + i * 64 + j] = OT::from_f(acc[r]);
+        out[IO::kP + frag_off<KK>(i, j, 64)] = OT::from_f(acc[r]);
       }
     }
   }
@@ -502,8 +504,8 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
       if (active) {
         const u32x4_t b0 = {ke0[4 * v], ke0[4 * v + 1], ke0[4 * v + 2], ke0[4 * v + 3]};
         const u32x4_t b1 = {ke1[4 * v], ke1[4 * v + 1], ke1[4 * v + 2], ke1[4 * v + 3]};
-        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + c0 * 64 + r0 + 8 * v) = b0;
-        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + (c0 + 1) * 64 + r0 + 8 * v) = b1;
+        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + frag_off<32>(c0, r0 + 8 * v, 64)) = b0;
+        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + frag_off<32>(c0 + 1, r0 + 8 * v, 64)) = b1;
       }
     }
     if (active && tp == 0) {
@@ -632,10 +634,17 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
       const uint16_t v = f32_to_bf16(tv[q]);
       Tb[i * LDC + j] = v;
       TbT[j * LDC + i] = v;
-      if (active) out[IO::kT + i * 64 + j] = v;
     }
   }
   __syncthreads();
+  if (active) {  // T to global in fragment-major order: 16-byte runs of 8 columns
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int cidx = t + 256 * q, i = cidx >> 3, j0 = (cidx & 7) * 8;
+      *reinterpret_cast<u16x8*>(out + IO::kT + frag_off<32>(i, j0, 64)) =
+          *reinterpret_cast<const u16x8*>(Tb + i * LDC + j0);
+    }
+  }
 
   // ---- F: Keff^T = Kt^T T^T  (M = channels, N = tokens; T lower triangular) ---
   constexpr int MTW = D / 64;  // channel tiles per wave
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
         u16x4 w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(kacc[u][nt][r]);
-        *reinterpret_cast<u16x4*>(out + IO::kKeff + tok * D + ch) = w;
+        *reinterpret_cast<u16x4*>(out + IO::kKeff + frag_off<32>(tok, ch, D)) = w;
       }
     }
   }
@@ -684,7 +693,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
         u16x4 w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(bf16_to_f32(qv[r]) - acc[r]);
-        *reinterpret_cast<u16x4*>(out + IO::kQeff + tok * D + ch) = w;
+        *reinterpret_cast<u16x4*>(out + IO::kQeff + frag_off<32>(tok, ch, D)) = w;
       }
     }
   }
@@ -703,7 +712,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
         u16x4 w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(acc[r]);
-        *reinterpret_cast<u16x4*>(out + IO::kP + tok * 64 + col) = w;
+        *reinterpret_cast<u16x4*>(out + IO::kP + frag_off<32>(tok, col, 64)) = w;
       }
     }
   }
@@ -759,14 +768,14 @@ __device__ __forceinline__ void load_ops(ChunkOps<D, Op>& f, const ScanCtx& c, i
   const Op* pa = blk + (c.is_o ? IO::kP : IO::kT);
   const Op* pb = blk + (c.is_o ? IO::kQeff : IO::kKeff);
 #pragma unroll
-  for (int i = 0; i < CO::NKC; ++i) f.fa[i] = frag<Op>(pa, 64, 16 * rt, i * CO::KK, c.lane);
+  for (int i = 0; i < CO::NKC; ++i) f.fa[i] = frag_fm<Op>(pa, rt, i, 64, c.lane);
 #pragma unroll
-  for (int i = 0; i < CO::NKD; ++i) f.fb[i] = frag<Op>(pb, D, 16 * rt, i * CO::KK, c.lane);
+  for (int i = 0; i < CO::NKD; ++i) f.fb[i] = frag_fm<Op>(pb, rt, i, D, c.lane);
   {  // unconditional (a wave without an S tile reads a valid row it ignores)
     const int srow = min(16 * c.wv, D - 16);
 #pragma unroll
     for (int i = 0; i < CO::NKC; ++i)
-      f.fe[i] = frag<Op>(blk + IO::kKendT, 64, srow, i * CO::KK, c.lane);
+      f.fe[i] = frag_fm<Op>(blk + IO::kKendT, srow >> 4, i, 64, c.lane);
     const float* gam = reinterpret_cast<const float*>(blk + IO::kGammaElems);
     f.gam = *reinterpret_cast<const f32x4*>(gam + srow + 4 * (c.lane >> 4));
   }
