@@ -22,6 +22,7 @@
 // slab of S in fp32 registers.  Column j of S depends only on column j of v,
 // which is what allows the d_v split.  A partial final chunk is padded with
 // zero rows (k = q = v = g = beta = 0), which leave the state unchanged.
+#include <cstdlib>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -727,25 +728,30 @@ constexpr int kBV = 16;  // value columns per slab
 // Workgroup id -> (pair, slab): the NS slabs of one (sequence, head) pair get
 // ids congruent modulo 8, so they are dispatched to the same XCD and share its
 // L2 for the pair's chunk intermediates.
-template <int D> struct ScanGrid {
-  static constexpr int NS = D / kBV;
+template <int D, int NH> struct ScanGrid {
+  static constexpr int NS = D / (kBV * NH);
   __host__ __device__ static int grid(int npairs) { return 8 * NS * ((npairs + 7) / 8); }
 };
 
-// Scan workgroup: 8 waves on one (sequence, head, 16-column slab).
+// Scan workgroup: 8 waves on one (sequence, head, slab of 16*NH value columns).
 //   waves 0-3 ("W"): rows 16w..16w+15 of W = T V - Keff S          -> LDS
 //   waves 4-7 ("O"): the same rows of O, formed transposed,
 //                    O^T = V^T P^T + S^T Qeff^T, stored as 4-column runs
 //   every wave that owns an S tile (rows 16w..16w+15) applies
 //                    S <- diag(gamma_C) S + Kend^T W.
+// Each operand fragment feeds NH MFMAs (one per 16-column half), so a wider
+// slab (NH = 2) halves the L2 traffic per column at twice the work per wave.
 // Operands of chunk n+PF are loaded into registers while chunk n computes.
-template <int D, typename Op> struct ChunkOps {
+template <int D, typename Op, int NH> struct ChunkOps {
   static constexpr int KK = OpT<Op>::kK, NKD = D / KK, NKC = 64 / KK;
   Frag<Op> fa[NKC];  // W waves: T rows; O waves: P rows
   Frag<Op> fb[NKD];  // W waves: Keff rows; O waves: Qeff rows
   Frag<Op> fe[NKC];  // Kend^T rows of the wave's S tile
   f32x4 gam;         // gamma_C of the 4 S rows this lane holds
-  typename std::conditional<sizeof(Op) == 2, uint32_t, u32x2_t>::type vraw;  // 2 V values
+  // 2*NH V values of this thread, kept in the input encoding until used
+  typename std::conditional<sizeof(Op) == 2,
+                            typename std::conditional<NH == 1, uint32_t, u32x2_t>::type,
+                            typename std::conditional<NH == 1, u32x2_t, u32x4_t>::type>::type vraw;
 };
 
 struct ScanCtx {
@@ -758,9 +764,9 @@ struct ScanCtx {
   int len, chunk_begin;
 };
 
-template <int D, typename Op>
-__device__ __forceinline__ void load_ops(ChunkOps<D, Op>& f, const ScanCtx& c, int n) {
-  using CO = ChunkOps<D, Op>;
+template <int D, typename Op, int NH>
+__device__ __forceinline__ void load_ops(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
+  using CO = ChunkOps<D, Op, NH>;
   using IO = InterOff<D>;
   const Op* blk = reinterpret_cast<const Op*>(
       c.inter + ((int64_t)(c.chunk_begin + n) * c.H + c.h) * c.blk_bytes);
@@ -774,8 +780,7 @@ __device__ __forceinline__ void load_ops(ChunkOps<D, Op>& f, const ScanCtx& c, i
   {  // unconditional (a wave without an S tile reads a valid row it ignores)
     const int srow = min(16 * c.wv, D - 16);
 #pragma unroll
-    for (int i = 0; i < CO::NKC; ++i)
-      f.fe[i] = frag_fm<Op>(blk + IO::kKendT, srow >> 4, i, 64, c.lane);
+    for (int i = 0; i < CO::NKC; ++i) f.fe[i] = frag_fm<Op>(blk + IO::kKendT, srow >> 4, i, 64, c.lane);
     const float* gam = reinterpret_cast<const float*>(blk + IO::kGammaElems);
     f.gam = *reinterpret_cast<const f32x4*>(gam + srow + 4 * (c.lane >> 4));
   }
@@ -786,17 +791,17 @@ __device__ __forceinline__ void load_ops(ChunkOps<D, Op>& f, const ScanCtx& c, i
   f.vraw = *reinterpret_cast<const VR*>(vp);  // rows past the chunk end are zeroed at use
 }
 
-template <int D, typename Op>
+template <int D, typename Op, int NH>
 __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   using OT = OpT<Op>;
-  using CO = ChunkOps<D, Op>;
-  constexpr int NS = D / kBV, KK = OT::kK;
+  using CO = ChunkOps<D, Op, NH>;
+  constexpr int BW = 16 * NH, NS = D / BW, KK = OT::kK;
   constexpr int PF = sizeof(Op) == 2 ? 3 : 1;  // chunks of operands prefetched ahead
   constexpr int PAD = 16 / (int)sizeof(Op);
   constexpr int LDS_ = D + PAD, LDW = 64 + PAD;
-  __shared__ __align__(16) Op Sb[kBV * LDS_];  // S^T slab [col][row]
-  __shared__ __align__(16) Op Wb[kBV * LDW];   // W^T [col][token]
-  __shared__ __align__(16) Op Vb[kBV * LDW];   // V^T [col][token]
+  __shared__ __align__(16) Op Sb[BW * LDS_];  // S^T slab [col][row]
+  __shared__ __align__(16) Op Wb[BW * LDW];   // W^T [col][token]
+  __shared__ __align__(16) Op Vb[BW * LDW];   // V^T [col][token]
 
   const int L = blockIdx.x;
   const int xcd = L & 7, slab = (L >> 3) % NS, blk = L / (8 * NS);
@@ -811,11 +816,11 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   c.v = a.v;
   c.H = H;
   c.h = h;
-  c.c0 = slab * kBV;
+  c.c0 = slab * BW;
   c.wv = wv;
   c.lane = lane;
-  c.vt = tid >> 3;       // V tile: token
-  c.vc = (tid & 7) * 2;  // V tile: column pair
+  c.vt = tid >> 3;            // V tile: token
+  c.vc = (tid & 7) * 2 * NH;  // V tile: first of 2*NH columns
   c.is_o = wv >= 4;
   c.owns_s = 16 * wv < D;
   c.row_begin = se.row_begin;
@@ -825,27 +830,34 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   const int64_t hoff = (int64_t)h * D * D;
   const int nchunks = (se.len + 63) / 64;
 
-  ChunkOps<D, Op> f0, f1, f2, f3;
+  CO f0, f1, f2, f3;
   if (nchunks > 0) {
-    load_ops<D, Op>(f0, c, 0);
-    if (PF >= 2) load_ops<D, Op>(f1, c, min(1, nchunks - 1));
-    if (PF >= 3) load_ops<D, Op>(f2, c, min(2, nchunks - 1));
+    load_ops<D, Op, NH>(f0, c, 0);
+    if (PF >= 2) load_ops<D, Op, NH>(f1, c, min(1, nchunks - 1));
+    if (PF >= 3) load_ops<D, Op, NH>(f2, c, min(2, nchunks - 1));
   }
 
-  // this wave's S tile: rows 16*wv + 4*(lane/16) + r, column c0 + lane%16
-  f32x4 S = zero4();
+  // this wave's S tiles: rows 16*wv + 4*(lane/16) + r, column c0 + 16*j + lane%16
+  f32x4 S[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) S[j] = zero4();
   if (c.owns_s && se.state_in >= 0) {
     const float* src = reinterpret_cast<const float*>(a.pool + se.state_in * a.page_bytes) + hoff;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[r] = src[(16 * wv + acc_row(lane, r)) * D + c.c0 + acc_col(lane)];
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[j][r] = src[(16 * wv + acc_row(lane, r)) * D + c.c0 + 16 * j + acc_col(lane)];
   }
   auto s_to_lds = [&]() {
     if (c.owns_s) {
-      if constexpr (sizeof(Op) == 2) {
-        *reinterpret_cast<u16x4*>(Sb + acc_col(lane) * LDS_ + 16 * wv + acc_row(lane, 0)) =
-            pack_bf16x4(S[0], S[1], S[2], S[3]);
-      } else {
-        *reinterpret_cast<f32x4*>(Sb + acc_col(lane) * LDS_ + 16 * wv + acc_row(lane, 0)) = S;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        Op* d = Sb + (16 * j + acc_col(lane)) * LDS_ + 16 * wv + acc_row(lane, 0);
+        if constexpr (sizeof(Op) == 2)
+          *reinterpret_cast<u16x4*>(d) = pack_bf16x4(S[j][0], S[j][1], S[j][2], S[j][3]);
+        else
+          *reinterpret_cast<f32x4*>(d) = S[j];
       }
     }
   };
@@ -853,7 +865,10 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
     if (c.owns_s) {
       float* dst = reinterpret_cast<float*>(a.pool + page * a.page_bytes) + hoff;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * wv + acc_row(lane, r)) * D + c.c0 + acc_col(lane)] = S[r];
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dst[(16 * wv + acc_row(lane, r)) * D + c.c0 + 16 * j + acc_col(lane)] = S[j][r];
     }
   };
   s_to_lds();
@@ -862,54 +877,68 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   int64_t next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
 
   auto step = [&](CO& cur, CO& pre, int n) {
-    load_ops<D, Op>(pre, c, min(n + PF, nchunks - 1));
+    load_ops<D, Op, NH>(pre, c, min(n + PF, nchunks - 1));
     const int len = min(64, se.len - 64 * n);
     {  // V tile -> Vb (transposed), rows past the chunk end as zeros
       const bool live = c.vt < len;
-      if constexpr (sizeof(Op) == 2) {
-        Vb[c.vc * LDW + c.vt] = live ? (uint16_t)(cur.vraw & 0xffffu) : (uint16_t)0;
-        Vb[(c.vc + 1) * LDW + c.vt] = live ? (uint16_t)(cur.vraw >> 16) : (uint16_t)0;
-      } else {
-        Vb[c.vc * LDW + c.vt] = live ? __uint_as_float(cur.vraw[0]) : 0.f;
-        Vb[(c.vc + 1) * LDW + c.vt] = live ? __uint_as_float(cur.vraw[1]) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 2 * NH; ++j) {
+        Op x;
+        if constexpr (sizeof(Op) == 2) {
+          if constexpr (NH == 1) x = (uint16_t)(cur.vraw >> (16 * j));
+          else x = (uint16_t)(cur.vraw[j >> 1] >> (16 * (j & 1)));
+        } else {
+          x = __uint_as_float(cur.vraw[j]);
+        }
+        Vb[(c.vc + j) * LDW + c.vt] = live ? x : Op(0);
       }
     }
     __syncthreads();  // Vb and Sb ready
 
     if (!c.is_o) {
-      f32x4 U = zero4(), X = zero4();
 #pragma unroll
-      for (int i = 0; i < CO::NKC; ++i) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 0, i * KK, lane));
+      for (int j = 0; j < NH; ++j) {
+        f32x4 U = zero4(), X = zero4();
 #pragma unroll
-      for (int i = 0; i < CO::NKD; ++i) mfma(X, cur.fb[i], frag<Op>(Sb, LDS_, 0, i * KK, lane));
-      Op* wdst = Wb + acc_col(lane) * LDW + 16 * rt + acc_row(lane, 0);
-      if constexpr (sizeof(Op) == 2) {
-        *reinterpret_cast<u16x4*>(wdst) = pack_bf16x4(U[0] - X[0], U[1] - X[1], U[2] - X[2], U[3] - X[3]);
-      } else {
-        *reinterpret_cast<f32x4*>(wdst) = U - X;
+        for (int i = 0; i < CO::NKC; ++i) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 16 * j, i * KK, lane));
+#pragma unroll
+        for (int i = 0; i < CO::NKD; ++i) mfma(X, cur.fb[i], frag<Op>(Sb, LDS_, 16 * j, i * KK, lane));
+        Op* wdst = Wb + (16 * j + acc_col(lane)) * LDW + 16 * rt + acc_row(lane, 0);
+        if constexpr (sizeof(Op) == 2)
+          *reinterpret_cast<u16x4*>(wdst) =
+              pack_bf16x4(U[0] - X[0], U[1] - X[1], U[2] - X[2], U[3] - X[3]);
+        else
+          *reinterpret_cast<f32x4*>(wdst) = U - X;
       }
     } else {
-      f32x4 OT4 = zero4();  // O^T[col = 4*(lane/16) + r][token = 16*rt + lane%16]
-#pragma unroll
-      for (int i = 0; i < CO::NKC; ++i) mfma(OT4, frag<Op>(Vb, LDW, 0, i * KK, lane), cur.fa[i]);
-#pragma unroll
-      for (int i = 0; i < CO::NKD; ++i) mfma(OT4, frag<Op>(Sb, LDS_, 0, i * KK, lane), cur.fb[i]);
       const int tok = 16 * rt + acc_col(lane);
-      if (tok < len) {
-        const int64_t base = ((c.row_begin + 64LL * n + tok) * H + h) * D + c.c0 + acc_row(lane, 0);
-        if (a.out_bf16)
-          *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + base) =
-              pack_bf16x4(OT4[0], OT4[1], OT4[2], OT4[3]);
-        else
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + base) = OT4;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        f32x4 OT4 = zero4();  // O^T[col = 16j + 4*(lane/16) + r][token = 16*rt + lane%16]
+#pragma unroll
+        for (int i = 0; i < CO::NKC; ++i) mfma(OT4, frag<Op>(Vb, LDW, 16 * j, i * KK, lane), cur.fa[i]);
+#pragma unroll
+        for (int i = 0; i < CO::NKD; ++i) mfma(OT4, frag<Op>(Sb, LDS_, 16 * j, i * KK, lane), cur.fb[i]);
+        if (tok < len) {
+          const int64_t base =
+              ((c.row_begin + 64LL * n + tok) * H + h) * D + c.c0 + 16 * j + acc_row(lane, 0);
+          if (a.out_bf16)
+            *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + base) =
+                pack_bf16x4(OT4[0], OT4[1], OT4[2], OT4[3]);
+          else
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + base) = OT4;
+        }
       }
     }
     __syncthreads();  // Wb ready; every wave is done reading Sb and Vb
 
     if (c.owns_s) {  // S <- diag(gamma_C) S + Kend^T W
-      S *= cur.gam;
 #pragma unroll
-      for (int i = 0; i < CO::NKC; ++i) mfma(S, cur.fe[i], frag<Op>(Wb, LDW, 0, i * KK, lane));
+      for (int j = 0; j < NH; ++j) {
+        S[j] *= cur.gam;
+#pragma unroll
+        for (int i = 0; i < CO::NKC; ++i) mfma(S[j], cur.fe[i], frag<Op>(Wb, LDW, 16 * j, i * KK, lane));
+      }
     }
     if (se.start_pos + 64LL * n + len == next_pos) {
       s_store(a.ckpts[nck].page);
@@ -961,9 +990,10 @@ static hipError_t launch_prep_t(const PrepArgs& a, int total_chunks, hipStream_t
   return hipGetLastError();
 }
 
-template <int D, typename Op>
+template <int D, typename Op, int NH>
 static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((scan_kernel<D, Op>), dim3(ScanGrid<D>::grid(a.npairs)), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((scan_kernel<D, Op, NH>), dim3(ScanGrid<D, NH>::grid(a.npairs)), dim3(512), 0,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -982,13 +1012,23 @@ hipError_t launch_prep(int D, bool bf16, const PrepArgs& a, int total_chunks, hi
   return D == 128 ? launch_prep_t<128, float>(a, total_chunks, st) : launch_prep_t<64, float>(a, total_chunks, st);
 }
 
-hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st) {
-  if (D == 128) return bf16 ? launch_scan_t<128, uint16_t>(a, st) : launch_scan_t<128, float>(a, st);
-  return bf16 ? launch_scan_t<64, uint16_t>(a, st) : launch_scan_t<64, float>(a, st);
+// Slab width: 32 value columns when that still gives every CU a slab (fewer,
+// wider slabs halve the L2 traffic per column), else 16.
+int scan_slab_halves(int D, int npairs) {
+  const char* env = getenv("KDA_SCAN_SLAB");
+  if (env && (env[0] == '1' || env[0] == '2')) return env[0] - '0';
+  return (long long)npairs * (D / 32) >= 256 ? 2 : 1;
 }
 
-int scan_grid(int D, int npairs) {
-  return D == 128 ? ScanGrid<128>::grid(npairs) : ScanGrid<64>::grid(npairs);
+hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st) {
+  const int nh = scan_slab_halves(D, a.npairs);
+  if (D == 128) {
+    if (bf16) return nh == 2 ? launch_scan_t<128, uint16_t, 2>(a, st) : launch_scan_t<128, uint16_t, 1>(a, st);
+    return nh == 2 ? launch_scan_t<128, float, 2>(a, st) : launch_scan_t<128, float, 1>(a, st);
+  }
+  if (bf16) return nh == 2 ? launch_scan_t<64, uint16_t, 2>(a, st) : launch_scan_t<64, uint16_t, 1>(a, st);
+  return nh == 2 ? launch_scan_t<64, float, 2>(a, st) : launch_scan_t<64, float, 1>(a, st);
 }
+
 
 }  // namespace kda
