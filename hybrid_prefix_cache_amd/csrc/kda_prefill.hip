@@ -382,7 +382,8 @@ template <int D> struct Prep2Layout {
   static constexpr int kRT = kRQ + kTileK;
   static constexpr int kRTBytes = (D * LDC * 2 > TPARTS * D * 4) ? D * LDC * 2 : TPARTS * D * 4;
   static constexpr int kRAQ = kRT + kRTBytes;
-  static constexpr int kHalf = kRAQ + 64 * LDC * 2;
+  static constexpr int kBeta = kRAQ + 64 * LDC * 2;  // fp32 beta[64]
+  static constexpr int kHalf = kBeta + 64 * 4;
   static_assert(kHalf <= 80 * 1024, "two pairs must fit in one CU's LDS");
   static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kRAQ % 16 == 0 && kHalf % 16 == 0, "align");
 };
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
   uint16_t* KtT = reinterpret_cast<uint16_t*>(base + LY::kRT);
   uint16_t* KeffT = KtT;
   uint16_t* Aq = reinterpret_cast<uint16_t*>(base + LY::kRAQ);
+  float* beta_s = reinterpret_cast<float*>(base + LY::kBeta);
 
   const int pair = 2 * blockIdx.x + half;
   const bool active = pair < total_pairs;  // an idle half still joins every barrier
@@ -440,6 +442,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
     gq2[i] = ok ? *reinterpret_cast<const uint32_t*>(gq + off) : 0u;
     gg2[i] = ok ? *reinterpret_cast<const uint32_t*>(gg + off) : 0u;
   }
+  if (t < 64) beta_s[t] = (active && t < len) ? bf16_to_f32(gb[(row0 + t) * H + h]) : 0.f;
 
   // ---- B: inclusive prefix sum of g over tokens (registers + run totals) ----
   float G0[TPP], G1[TPP];
@@ -518,36 +521,39 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
   __syncthreads();
 
   // ---- D: Gram matrices (waves 0,1: Kt Kh^T; waves 2,3: Qt Kh^T) --------------
+  // each wave takes block rows {0,3} or {1,2}; a row's A fragments are loaded
+  // once and reused for every tile of the row
   {
     const int gram = wv >> 1;
     const uint16_t* Aop = gram == 0 ? Kt : Qt;
+    constexpr int NKD = D / 32;
     f32x4 acc[2][4];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       const int mt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
+      Frag<uint16_t> af[NKD];
+#pragma unroll
+      for (int i = 0; i < NKD; ++i) af[i] = frag<uint16_t>(Aop, LDK, 16 * mt, 32 * i, lane);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         acc[pass][nt] = zero4();
-        if (nt <= mt) tile_mma<uint16_t>(acc[pass][nt], Aop, LDK, 16 * mt, Kh, LDK, 16 * nt, 0, D, lane);
+        if (nt <= mt) {
+#pragma unroll
+          for (int i = 0; i < NKD; ++i) mfma(acc[pass][nt], af[i], frag<uint16_t>(Kh, LDK, 16 * nt, 32 * i, lane));
+        }
       }
     }
     __syncthreads();  // Kt/Kh are overwritten by L below
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       const int mt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
-      float br[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mt + acc_row(lane, r);
-        br[r] = (active && i < len) ? bf16_to_f32(gb[(row0 + i) * H + h]) : 0.f;
-      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
           if (gram == 0) {
-            if (nt <= mt) Lm[i * LDF + j] = (j < i) ? br[r] * acc[pass][nt][r] : 0.f;
+            if (nt <= mt) Lm[i * LDF + j] = (j < i) ? beta_s[i] * acc[pass][nt][r] : 0.f;
           } else {
             Aq[i * LDC + j] = f32_to_bf16((j <= i) ? acc[pass][nt][r] : 0.f);
           }
@@ -557,9 +563,14 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
   }
   __syncthreads();
 
-  // ---- E: T = (I + L)^-1 diag(beta) by 16x16 blocks ----------------------------
-  if (lane < 16) {
-    const int j = lane, b0 = 16 * wv;
+  // ---- E: Tinv = (I + L)^-1 by 16x16 blocks, then T = Tinv diag(beta) -------
+  // 1) wave 0 inverts the four diagonal blocks at once: lane = 16*block + column
+  //    runs the column's forward substitution;
+  // 2) 32x32 merges on fp32 MFMA: X10 = -N1 (L10 N0), X32 = -N3 (L32 N2);
+  // 3) 64x64 merge: Y = L[32:64, 0:32] Inv_A, X = -Inv_B Y, where
+  //    Inv_A = [[N0, 0], [X10, N1]] and Inv_B = [[N2, 0], [X32, N3]].
+  if (wv == 0) {
+    const int b0 = 16 * (lane >> 4), j = lane & 15;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -572,56 +583,42 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
     for (int i = 0; i < 16; ++i) Ti[(b0 + i) * LDF + b0 + j] = x[i];
   }
   __syncthreads();
-  for (int ar = 1; ar < 4; ++ar) {
-    // Y_b = sum_{c=b}^{ar-1} L_{ar,c} X_{c,b}, staged in the destination block
-    float y[3];
+  // C tile (16x16) -> Ti block (row block rb, col block cb), optionally negated
+  auto put = [&](const f32x4& v, int rb, int cb, float sgn) {
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int it = t + 256 * q;
-      y[q] = 0.f;
-      if (it < ar * 256) {
-        const int b = it >> 8, i = (it >> 4) & 15, j = it & 15;
-        float acc = 0.f;
-        for (int c = b; c < ar; ++c)
-#pragma unroll
-          for (int m = 0; m < 16; ++m)
-            acc += Lm[(16 * ar + i) * LDF + 16 * c + m] * Ti[(16 * c + m) * LDF + 16 * b + j];
-        y[q] = acc;
-        Ti[(16 * ar + i) * LDF + 16 * b + j] = acc;
-      }
-    }
-    __syncthreads();
-    float x[3];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int it = t + 256 * q;
-      x[q] = 0.f;
-      if (it < ar * 256) {
-        const int b = it >> 8, i = (it >> 4) & 15, j = it & 15;
-        float acc = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          acc += Ti[(16 * ar + i) * LDF + 16 * ar + m] * Ti[(16 * ar + m) * LDF + 16 * b + j];
-        x[q] = -acc;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int it = t + 256 * q;
-      if (it < ar * 256) {
-        const int b = it >> 8, i = (it >> 4) & 15, j = it & 15;
-        Ti[(16 * ar + i) * LDF + 16 * b + j] = x[q];
-      }
-    }
-    (void)y;
-    __syncthreads();
+    for (int r = 0; r < 4; ++r) Ti[(16 * rb + acc_row(lane, r)) * LDF + 16 * cb + acc_col(lane)] = sgn * v[r];
+  };
+  if (wv < 2) {  // level 1: wave 0 -> X10, wave 1 -> X32 (Y staged in place)
+    const int a0 = wv == 0 ? 1 : 3, b0 = a0 - 1;
+    f32x4 y = zero4();
+    tile_mma_kn(y, Lm, LDF, 16 * a0, Ti, LDF, 16 * b0, 16 * b0, 16 * b0 + 16, lane);  // L_ab N_b
+    put(y, a0, b0, 1.f);
+    f32x4 xx = zero4();
+    tile_mma_kn(xx, Ti, LDF, 16 * a0, Ti, LDF, 16 * b0, 16 * a0, 16 * a0 + 16, lane);  // N_a Y
+    put(xx, a0, b0, -1.f);  // reads of Y finished: the MFMA inputs are in registers
   }
+  __syncthreads();
+  {  // level 2, Y = C Inv_A: wave w -> block (2 + (w >> 1), w & 1)
+    const int ra = 2 + (wv >> 1), cb = wv & 1;
+    f32x4 y = zero4();
+    // Y_{ra,cb} = sum_{c = cb}^{1} L_{ra,c} Inv_A[c][cb]
+    tile_mma_kn(y, Lm, LDF, 16 * ra, Ti, LDF, 16 * cb, 16 * cb, 32, lane);
+    put(y, ra, cb, 1.f);
+  }
+  __syncthreads();
+  {  // X = -Inv_B Y: X_{ra,cb} = -sum_{c = 2}^{ra} Inv_B[ra][c] Y_{c,cb}
+    const int ra = 2 + (wv >> 1), cb = wv & 1;
+    f32x4 xx = zero4();
+    tile_mma_kn(xx, Ti, LDF, 16 * ra, Ti, LDF, 16 * cb, 32, 16 * ra + 16, lane);
+    __syncthreads();  // every wave has read its Y blocks
+    put(xx, ra, cb, -1.f);
+  }
+  __syncthreads();
   {
     // T[i][j] = Tinv[i][j] beta_j (j <= i); thread t owns column j = t & 63,
     // rows i = (t >> 6) + 4 q
     const int j = t & 63;
-    const float bj = (active && j < len) ? bf16_to_f32(gb[(row0 + j) * H + h]) : 0.f;
+    const float bj = beta_s[j];
     float tv[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
