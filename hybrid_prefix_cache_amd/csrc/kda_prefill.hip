@@ -149,7 +149,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   float* beta_s = reinterpret_cast<float*>(smem + LY::kBeta);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x, h = blockIdx.y, H = a.H;
+  // chunks in reverse dispatch order (see prep2_kernel)
+  const int chunk = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, H = a.H;
   const SeqEntry se = a.seqs[find_seq(a.seqs, a.num_seqs, chunk)];
   const int lc = chunk - se.chunk_begin;
   const int64_t row0 = se.row_begin + 64LL * lc;
@@ -356,15 +357,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// prep for bf16 inputs: two (chunk, head) pairs per 512-thread workgroup
+// prep for bf16 inputs: one (chunk, head) pair per 256-thread workgroup
 // ---------------------------------------------------------------------------
-// Each half of the workgroup (4 waves) owns one pair and an LDS region of at
-// most 80 KB whose parts are reused phase by phase:
+// The workgroup (4 waves) owns an LDS region of at most 80 KB whose parts are
+// reused phase by phase:
 //   RA : Kt | Kh (decayed keys)  ->  L | Tinv (fp32 solve)  ->  T | T^T (bf16)
 //   RQ : Qt (decayed queries)
 //   RT : prefix partials  ->  Kt^T (keys, token-contiguous)  ->  Keff^T
 //   RAQ: Aq (masked Qt Kh^T)
-// so two pairs share a CU and their phases interleave on the SIMDs.
+// so two workgroups share a CU and their phases interleave on the SIMDs (two
+// independent workgroups beat one workgroup holding both pairs in lockstep).
 // Element-wise work maps thread -> (channel pair, run of tokens), giving
 // 256-byte coalesced loads and a register prefix sum; products are formed
 // transposed (M = channels) so results reach global memory as 8-byte runs.
@@ -383,22 +385,22 @@ template <int D> struct Prep2Layout {
   static constexpr int kRTBytes = (D * LDC * 2 > TPARTS * D * 4) ? D * LDC * 2 : TPARTS * D * 4;
   static constexpr int kRAQ = kRT + kRTBytes;
   static constexpr int kBeta = kRAQ + 64 * LDC * 2;  // fp32 beta[64]
-  static constexpr int kHalf = kBeta + 64 * 4;
-  static_assert(kHalf <= 80 * 1024, "two pairs must fit in one CU's LDS");
-  static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kRAQ % 16 == 0 && kHalf % 16 == 0, "align");
+  static constexpr int kBytes = kBeta + 64 * 4;
+  static_assert(kBytes <= 80 * 1024, "two workgroups must fit in one CU's LDS");
+  static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kRAQ % 16 == 0 && kBytes % 16 == 0, "align");
 };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
 
 template <int D>
-__global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs) {
+__global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs) {
   using LY = Prep2Layout<D>;
   using IO = InterOff<D>;
   constexpr int NP = LY::NP, TPP = LY::TPP, LDK = LY::LDK, LDC = LY::LDC, LDF = LY::LDF;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int half = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6;
-  uint8_t* base = smem + half * LY::kHalf;
+  uint8_t* base = smem;
   uint16_t* Kt = reinterpret_cast<uint16_t*>(base + LY::kRA);
   uint16_t* Kh = Kt + 64 * LDK;
   float* Lm = reinterpret_cast<float*>(base + LY::kRA);
@@ -412,18 +414,16 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
   uint16_t* Aq = reinterpret_cast<uint16_t*>(base + LY::kRAQ);
   float* beta_s = reinterpret_cast<float*>(base + LY::kBeta);
 
-  const int pair = 2 * blockIdx.x + half;
-  const bool active = pair < total_pairs;  // an idle half still joins every barrier
+  // Pairs are taken in reverse order: the scan reads chunks first to last, so
+  // the blocks written last (the earliest chunks) are the ones still resident
+  // in the memory-side cache when it starts, instead of the ones evicted first.
+  const int pair = total_pairs - 1 - (int)blockIdx.x;
   const int H = a.H;
-  const int chunk = active ? pair / H : 0, h = active ? pair % H : 0;
-  int len = 0;
-  int64_t row0 = 0;
-  if (active) {
-    const SeqEntry se = a.seqs[find_seq(a.seqs, a.num_seqs, chunk)];
-    const int lc = chunk - se.chunk_begin;
-    row0 = se.row_begin + 64LL * lc;
-    len = min(64, se.len - 64 * lc);
-  }
+  const int chunk = pair / H, h = pair % H;
+  const SeqEntry se = a.seqs[find_seq(a.seqs, a.num_seqs, chunk)];
+  const int lc = chunk - se.chunk_begin;
+  const int64_t row0 = se.row_begin + 64LL * lc;
+  const int len = min(64, se.len - 64 * lc);
   const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* gk = reinterpret_cast<const uint16_t*>(a.k);
   const uint16_t* gg = reinterpret_cast<const uint16_t*>(a.g);
@@ -436,13 +436,13 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
 #pragma unroll
   for (int i = 0; i < TPP; ++i) {
     const int r = r0 + i;
-    const bool ok = active && r < len;
+    const bool ok = r < len;
     const int64_t off = ((row0 + (ok ? r : 0)) * H + h) * D + c0;
     gk2[i] = ok ? *reinterpret_cast<const uint32_t*>(gk + off) : 0u;
     gq2[i] = ok ? *reinterpret_cast<const uint32_t*>(gq + off) : 0u;
     gg2[i] = ok ? *reinterpret_cast<const uint32_t*>(gg + off) : 0u;
   }
-  if (t < 64) beta_s[t] = (active && t < len) ? bf16_to_f32(gb[(row0 + t) * H + h]) : 0.f;
+  if (t < 64) beta_s[t] = t < len ? bf16_to_f32(gb[(row0 + t) * H + h]) : 0.f;
 
   // ---- B: inclusive prefix sum of g over tokens (registers + run totals) ----
   float G0[TPP], G1[TPP];
@@ -505,14 +505,14 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
       const u32x4_t a1 = {ktT1[4 * v], ktT1[4 * v + 1], ktT1[4 * v + 2], ktT1[4 * v + 3]};
       *reinterpret_cast<u32x4_t*>(KtT + c0 * LDC + r0 + 8 * v) = a0;
       *reinterpret_cast<u32x4_t*>(KtT + (c0 + 1) * LDC + r0 + 8 * v) = a1;
-      if (active) {
+      {
         const u32x4_t b0 = {ke0[4 * v], ke0[4 * v + 1], ke0[4 * v + 2], ke0[4 * v + 3]};
         const u32x4_t b1 = {ke1[4 * v], ke1[4 * v + 1], ke1[4 * v + 2], ke1[4 * v + 3]};
         *reinterpret_cast<u32x4_t*>(out + IO::kKendT + frag_off<32>(c0, r0 + 8 * v, 64)) = b0;
         *reinterpret_cast<u32x4_t*>(out + IO::kKendT + frag_off<32>(c0 + 1, r0 + 8 * v, 64)) = b1;
       }
     }
-    if (active && tp == 0) {
+    if (tp == 0) {
       float* gamma = reinterpret_cast<float*>(out + IO::kGammaElems);
       gamma[c0] = eC0;
       gamma[c0 + 1] = eC1;
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
     }
   }
   __syncthreads();
-  if (active) {  // T to global in fragment-major order: 16-byte runs of 8 columns
+  {  // T to global in fragment-major order: 16-byte runs of 8 columns
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int cidx = t + 256 * q, i = cidx >> 3, j0 = (cidx & 7) * 8;
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
       kacc[u][nt] = zero4();
       const int ke = nt < 2 ? 32 : 64;
       tile_mma<uint16_t>(kacc[u][nt], KtT, LDC, 16 * mt, Tb, LDC, 16 * nt, 0, ke, lane);
-      if (active) {  // Keff[tok][ch .. ch+3]: lane holds 4 consecutive channels of one token
+      {  // Keff[tok][ch .. ch+3]: lane holds 4 consecutive channels of one token
         const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
         u16x4 w;
 #pragma unroll
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
       f32x4 acc = zero4();
       const int ke = nt < 2 ? 32 : 64;
       tile_mma<uint16_t>(acc, KeffT, LDC, 16 * mt, Aq, LDC, 16 * nt, 0, ke, lane);
-      if (active) {
+      {
         const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
         const u16x4 qv = *reinterpret_cast<const u16x4*>(Qt + tok * LDK + ch);
         u16x4 w;
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(512) void prep2_kernel(PrepArgs a, int total_pairs)
         const int kb = (16 * mt) / 32 * 32, ke = nt < 2 ? 32 : 64;
         tile_mma<uint16_t>(acc, TbT, LDC, 16 * mt, Aq, LDC, 16 * nt, kb, ke, lane);
       }
-      if (active) {
+      {
         const int tok = 16 * nt + acc_col(lane), col = 16 * mt + acc_row(lane, 0);
         u16x4 w;
 #pragma unroll
@@ -761,19 +761,38 @@ struct ScanCtx {
   int len, chunk_begin;
 };
 
+// The operand loads of a future chunk are split in three groups issued at
+// different points of the current chunk, so the memory pipeline drains while
+// the waves compute instead of stalling them all at the top of the chunk.
+template <int D, typename Op>
+__device__ __forceinline__ const Op* chunk_block(const ScanCtx& c, int n) {
+  return reinterpret_cast<const Op*>(c.inter +
+                                     ((int64_t)(c.chunk_begin + n) * c.H + c.h) * c.blk_bytes);
+}
+
 template <int D, typename Op, int NH>
-__device__ __forceinline__ void load_ops(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
+__device__ __forceinline__ void load_ops_a(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
   using CO = ChunkOps<D, Op, NH>;
   using IO = InterOff<D>;
-  const Op* blk = reinterpret_cast<const Op*>(
-      c.inter + ((int64_t)(c.chunk_begin + n) * c.H + c.h) * c.blk_bytes);
-  const int rt = c.wv & 3;
-  const Op* pa = blk + (c.is_o ? IO::kP : IO::kT);
-  const Op* pb = blk + (c.is_o ? IO::kQeff : IO::kKeff);
+  const Op* pa = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kP : IO::kT);
 #pragma unroll
-  for (int i = 0; i < CO::NKC; ++i) f.fa[i] = frag_fm<Op>(pa, rt, i, 64, c.lane);
+  for (int i = 0; i < CO::NKC; ++i) f.fa[i] = frag_fm<Op>(pa, c.wv & 3, i, 64, c.lane);
+}
+
+template <int D, typename Op, int NH>
+__device__ __forceinline__ void load_ops_b(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
+  using CO = ChunkOps<D, Op, NH>;
+  using IO = InterOff<D>;
+  const Op* pb = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kQeff : IO::kKeff);
 #pragma unroll
-  for (int i = 0; i < CO::NKD; ++i) f.fb[i] = frag_fm<Op>(pb, rt, i, D, c.lane);
+  for (int i = 0; i < CO::NKD; ++i) f.fb[i] = frag_fm<Op>(pb, c.wv & 3, i, D, c.lane);
+}
+
+template <int D, typename Op, int NH>
+__device__ __forceinline__ void load_ops_c(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
+  using CO = ChunkOps<D, Op, NH>;
+  using IO = InterOff<D>;
+  const Op* blk = chunk_block<D, Op>(c, n);
   {  // unconditional (a wave without an S tile reads a valid row it ignores)
     const int srow = min(16 * c.wv, D - 16);
 #pragma unroll
@@ -786,6 +805,20 @@ __device__ __forceinline__ void load_ops(ChunkOps<D, Op, NH>& f, const ScanCtx& 
   const Op* vp = reinterpret_cast<const Op*>(c.v) +
                  ((c.row_begin + 64LL * n + min(c.vt, len - 1)) * c.H + c.h) * D + c.c0 + c.vc;
   f.vraw = *reinterpret_cast<const VR*>(vp);  // rows past the chunk end are zeroed at use
+}
+
+// Issued in the same group order as inside the chunk loop, with scheduling
+// fences, so that the wait counts the compiler derives at the loop entry
+// match the steady state (an interleaved prologue forces needlessly deep
+// waits on the first iterations of every unrolled group).
+template <int D, typename Op, int NH>
+__device__ __forceinline__ void load_ops(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
+  load_ops_a<D, Op, NH>(f, c, n);
+  __builtin_amdgcn_sched_barrier(0);
+  load_ops_b<D, Op, NH>(f, c, n);
+  __builtin_amdgcn_sched_barrier(0);
+  load_ops_c<D, Op, NH>(f, c, n);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D, typename Op, int NH>
@@ -874,7 +907,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   int64_t next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
 
   auto step = [&](CO& cur, CO& pre, int n) {
-    load_ops<D, Op, NH>(pre, c, min(n + PF, nchunks - 1));
+    const int nf = min(n + PF, nchunks - 1);  // chunk whose operands are prefetched
+    load_ops_a<D, Op, NH>(pre, c, nf);
+    __builtin_amdgcn_sched_barrier(0);
     const int len = min(64, se.len - 64 * n);
     {  // V tile -> Vb (transposed), rows past the chunk end as zeros
       const bool live = c.vt < len;
@@ -891,6 +926,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       }
     }
     __syncthreads();  // Vb and Sb ready
+    load_ops_b<D, Op, NH>(pre, c, nf);
+    __builtin_amdgcn_sched_barrier(0);
 
     if (!c.is_o) {
 #pragma unroll
@@ -928,6 +965,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       }
     }
     __syncthreads();  // Wb ready; every wave is done reading Sb and Vb
+    load_ops_c<D, Op, NH>(pre, c, nf);
+    __builtin_amdgcn_sched_barrier(0);
 
     if (c.owns_s) {  // S <- diag(gamma_C) S + Kend^T W
 #pragma unroll
@@ -996,11 +1035,11 @@ static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_prep2_t(const PrepArgs& a, int total_chunks, hipStream_t st) {
-  constexpr int kBytes = 2 * Prep2Layout<D>::kHalf;
+  constexpr int kBytes = Prep2Layout<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prep2_kernel<D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
   const int pairs = total_chunks * a.H;
-  hipLaunchKernelGGL((prep2_kernel<D>), dim3((pairs + 1) / 2), dim3(512), kBytes, st, a, pairs);
+  hipLaunchKernelGGL((prep2_kernel<D>), dim3(pairs), dim3(256), kBytes, st, a, pairs);
   return hipGetLastError();
 }
 
