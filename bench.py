@@ -15,8 +15,12 @@ Prints ONE JSON line (see the "roofline" and "cpu_baseline" fields).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,8 +45,82 @@ PREP_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 2
 SCAN_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2
 
 
+# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs over this
+# script, summarised by --summarize-pmc; valid only while the kernel source
+# still hashes to the value recorded with the counters.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_prefill8k_decode256_copy256.md")
+KERNEL_SOURCES = {"kda_prefill_prep": "kda_prefill.hip", "kda_prefill_scan": "kda_prefill.hip",
+                  "kda_decode_step": "kda_decode.hip", "kda_page_copy": "kda_copy.hip"}
+# device kernel symbol -> library launch name
+KERNEL_SYMBOLS = {"prep2_kernel": "kda_prefill_prep", "prep_kernel": "kda_prefill_prep",
+                  "scan_kernel": "kda_prefill_scan", "decode_kernel": "kda_decode_step",
+                  "copy_kernel": "kda_page_copy", "meta_fill_kernel": "kda_meta_fill"}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "hybrid_prefix_cache_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` recorded in the counter summary, or None
+    when there is none or the kernel source has changed since it was taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"^\| " + re.escape(kernel) + r" \| ([0-9a-f]{16}) \| [^|]* \| [^|]* \| ([0-9.e+]+) \|",
+                  text, re.M)
+    if not m or m.group(1) != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m.group(2))
+
+
+def summarize_pmc(fetch_dir, write_dir, command):
+    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, in
+    KiB per dispatch) of this script.  Each counter is scaled by the factor that
+    makes it read the known bytes of the page-copy kernel (256 pages of 2 MiB
+    read and written per launch)."""
+    def per_kernel(d, counter):
+        acc = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    sym = r["Kernel_Name"]
+                    name = next((v for k, v in KERNEL_SYMBOLS.items() if f"kda::{k}" in sym), None)
+                    if name:
+                        acc.setdefault(name, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = 256 * (2 << 20)
+    kf, kw = copy_bytes / fetch["kda_page_copy"], copy_bytes / write["kda_page_copy"]
+    lines = [
+        "# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+        "Workloads: prefill 8K x 32 heads x d=128 bf16 with 3 checkpoints; decode 256 requests x",
+        "32 heads; page copy 256 x 2 MiB.  Commands (from /tmp, TMPDIR=/tmp, R = repository root):", "",
+        "```", *command, "```", "",
+        f"Calibration against the page copy (512 MiB read + 512 MiB written per launch): "
+        f"FETCH_SIZE x {kf:.3f}, WRITE_SIZE x {kw:.3f}.  Source hash = first 16 hex digits of the",
+        "SHA-256 of the kernel's source file when the counters were taken; bench.py reports",
+        "`roofline.traffic` only while it still matches.", "",
+        "| kernel | source hash | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (calibrated) |",
+        "|---|---|---|---|---|",
+    ]
+    for name in sorted(set(fetch) & set(write)):
+        if name not in KERNEL_SOURCES:
+            continue
+        b = fetch[name] * kf + write[name] * kw
+        lines.append(f"| {name} | {source_hash(KERNEL_SOURCES[name])} | {fetch[name] / 1024:.0f} | "
+                     f"{write[name] / 1024:.0f} | {b:.6e} |")
+    return "\n".join(lines) + "\n"
 
 
 def to_dev(x, dtype):
@@ -170,7 +248,8 @@ def cpu_baseline(G, w, d):
     """The fp64 oracle on the same 8K workload (all 32 heads, all tokens), timed on
     this host's cores.  Generation is excluded."""
     import oracle
-    threads = os.cpu_count() or 1
+    # the host's CPU share (the scheduler affinity / OMP setting), not the machine total
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     oracle.run(d["q"], d["k"], d["v"], d["g"], d["beta"], [0, w.T], ckpt_cu=[0, len(w.ckpts)],
                ckpt_pos=list(w.ckpts), threads=threads)
@@ -187,7 +266,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only-prefill", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the markdown traffic summary of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        cmd = [f"rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{d} -o run -- "
+               f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu"
+               for c, d in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write"))]
+        cmd.append("python3 $R/bench.py --summarize-pmc $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write")
+        sys.stdout.write(summarize_pmc(*args.summarize_pmc, cmd))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
               f"--gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
@@ -224,7 +312,8 @@ def main():
                    "checkpoints": list(w.ckpts), "page_bytes": w.page_bytes,
                    "state_dtype": "f32", "io_dtype": "bf16"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic(dom),
                      "algorithmic_bytes_per_launch": alg[dom],
                      "avg_launch_ms": 1e3 * dom_s},
         "prefill_step": {"algorithmic_bytes": call_bytes, "algorithmic_flops": call_flops,
