@@ -12,6 +12,11 @@ import ctypes
 import os
 
 import numpy as np
+# torch first: it ships its own HIP runtime under the same soname as the one
+# libkda.so is linked against, and the first one loaded serves the whole
+# process.  Loading libkda first would pair torch with a runtime of another
+# ROCm release (kernel launches then fail with "no ROCm-capable device").
+import torch  # noqa: F401  (device memory and streams)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")

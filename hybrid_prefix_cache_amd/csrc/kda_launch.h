@@ -54,7 +54,7 @@ struct DecodeArgs {
 };
 
 constexpr int kCopyPairsPerLaunch = 448;
-constexpr int kPieceBytes = 64 * 1024;
+constexpr int kPieceBytes = 4096;  // bytes per copy workgroup: one 16-byte vector per thread
 
 struct CopyArgs {
   uint8_t* pool;
