@@ -182,7 +182,108 @@ def bench_prefill(K, G, steps, warmup):
 
     dev_s, wall_s = timed(step, steps, warmup)
     kt = kernel_times(K, step, max(steps, 5))
-    return w, d, dev_s, wall_s, kt
+    graph = bench_graph(step, w.T, steps, warmup)
+    return w, d, dev_s, wall_s, kt, graph
+
+
+def bench_graph(step, tokens, steps, warmup):
+    """The same prefill call captured once in a HIP graph and replayed: removes
+    the host-side validation and launch overhead from the timed loop."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        dev_s, _ = timed(g.replay, steps, warmup)
+    except Exception as e:  # reported, never hidden
+        return {"error": f"{type(e).__name__}: {e}"}
+    return {"ms_per_step": 1e3 * dev_s / steps, "tokens_per_s": tokens * steps / dev_s}
+
+
+def device_tokens(T, H, D, seed, dtype):
+    """q, k, v, g, beta drawn on the device with the generator's distributions
+    (q, k unit-norm per (token, head) from N(0,1); v N(0,1); g U[-0.05, 0);
+    beta sigmoid(N(0,1))), in slices so fp32 temporaries stay small.  Used where
+    host generation would take minutes; the values only feed timing."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {n: torch.empty((T, H, D), dtype=td, device="cuda") for n in ("q", "k", "v", "g")}
+    out["beta"] = torch.empty((T, H), dtype=td, device="cuda")
+    sl = 1 << 16
+    for t0 in range(0, T, sl):
+        n = min(sl, T - t0)
+        for name in ("q", "k"):
+            x = torch.randn((n, H, D), generator=gen, device="cuda")
+            out[name][t0:t0 + n] = (x / x.norm(dim=-1, keepdim=True)).to(td)
+        out["v"][t0:t0 + n] = torch.randn((n, H, D), generator=gen, device="cuda").to(td)
+        out["g"][t0:t0 + n] = (torch.rand((n, H, D), generator=gen, device="cuda") * -0.05).to(td)
+        out["beta"][t0:t0 + n] = torch.sigmoid(torch.randn((n, H), generator=gen, device="cuda")).to(td)
+    return out
+
+
+def bench_varlen(K, G, steps=20, warmup=3):
+    """Suffix prefill of the 16-sequence resume workload: each sequence restarts
+    at its 512-multiple boundary B from a state page and runs to its end, all
+    16 suffixes packed into one call."""
+    import torch
+    w = G.VARLEN_RESUME
+    lens, bnd = G.varlen_plan(w)
+    suf = (lens - bnd).astype(np.int64)
+    total = int(suf.sum())
+    d = G.kda_tokens(w.seed, w.H, w.D, 0, total, w.dtype)
+    di = {k: to_dev(v, w.dtype) for k, v in d.items()}
+    del d
+    sb = w.H * w.D * w.D * 4
+    n = w.n_seqs
+    pool_buf = torch.zeros(2 * n * sb // 4, dtype=torch.int32, device="cuda")
+    pool = K.make_pool(pool_buf, sb, 2 * n, w.H, w.D)
+    o = torch.empty((total, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_bytes(pool, total, n, 0, K.KDA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    cu = np.concatenate([[0], np.cumsum(suf)]).astype(np.int64)
+
+    def step():
+        K.kda_prefill_chunked(pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, cu,
+                              start_pos=bnd, state_in_page=list(range(n)),
+                              state_out_page=list(range(n, 2 * n)), workspace=ws)
+
+    dev_s, _ = timed(step, steps, warmup)
+    kt = kernel_times(K, step, steps)
+    return {"workload": w.name, "sequences": n, "suffix_tokens": total,
+            "ms_per_call": 1e3 * dev_s / steps, "tokens_per_s": total * steps / dev_s,
+            "kernels_avg_ms": {k: v["avg_ms"] for k, v in kt.items()}}
+
+
+def bench_long(K, G, steps=3, warmup=1):
+    """One 2^20-token sequence, 32 heads, 171 checkpoints written into the pool."""
+    import torch
+    w = G.LONG_1M
+    di = device_tokens(w.T, w.H, w.D, w.seed, w.dtype)
+    npg = len(w.ckpts) + 1
+    pool_buf = torch.zeros(npg * w.page_bytes // 4, dtype=torch.int32, device="cuda")
+    pool = K.make_pool(pool_buf, w.page_bytes, npg, w.H, w.D)
+    o = torch.empty((w.T, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(K.kda_prefill_workspace_bytes(pool, w.T, 1, len(w.ckpts), K.KDA_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        K.kda_prefill_chunked(pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, [0, w.T],
+                              ckpt_cu=[0, len(w.ckpts)], ckpt_pos=list(w.ckpts),
+                              ckpt_page=list(range(1, npg)), state_out_page=[0], workspace=ws)
+
+    dev_s, _ = timed(step, steps, warmup)
+    kt = kernel_times(K, step, steps)
+    return {"workload": w.name, "tokens": w.T, "checkpoints": len(w.ckpts),
+            "ms_per_call": 1e3 * dev_s / steps, "tokens_per_s": w.T * steps / dev_s,
+            "kernels_avg_ms": {k: v["avg_ms"] for k, v in kt.items()},
+            "inputs": "drawn on the device (seeded torch generator, the generator's distributions)"}
 
 
 def bench_decode(K, G, steps, warmup, n_inputs=32):
@@ -287,7 +388,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     log("prefill: generating inputs")
-    w, d, dev_s, wall_s, kt = bench_prefill(K, G, args.steps, args.warmup)
+    w, d, dev_s, wall_s, kt, graph = bench_prefill(K, G, args.steps, args.warmup)
     ms_step = 1e3 * dev_s / args.steps
     tok_s = w.T * args.steps / dev_s
     log(f"prefill: {ms_step:.3f} ms/step, {tok_s / 1e6:.2f} M tokens/s; kernels {kt}")
@@ -321,6 +422,7 @@ def main():
                          "frac_mfma_bf16": call_flops / step_s / 1e12 / BF16_PEAK_TFLOPS,
                          "wall_s": wall_s},
         "kernels": kt,
+        "prefill_graph": graph,
     }
     if not args.only_prefill:
         log("decode: 256 requests x 32 heads")
@@ -328,6 +430,14 @@ def main():
         log(f"decode: {out['decode']}")
         out["checkpoint_copy"] = bench_copy(K, steps=20, warmup=3)
         log(f"copy: {out['checkpoint_copy']}")
+        log("varlen resume: 16 sequences")
+        out["varlen_resume"] = bench_varlen(K, G)
+        log(f"varlen: {out['varlen_resume']}")
+        torch.cuda.empty_cache()
+        log("long: 2^20 tokens")
+        out["long_1m"] = bench_long(K, G)
+        log(f"long: {out['long_1m']}")
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         log("cpu baseline: oracle")
         out["cpu_baseline"] = cpu_baseline(G, w, d)

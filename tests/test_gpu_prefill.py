@@ -228,3 +228,47 @@ def test_long_1m():
     assert np.array_equal(pb.states(nck - 1), pb.states(nck))
     for m in range(0, nck, 17):
         assert np.all(np.isfinite(pb.states(m)))
+
+
+def test_graph_replay_bitwise():
+    """The prefill call captured once in a HIP graph (metadata travels in kernel
+    arguments, so nothing is re-validated at replay) and replayed three times,
+    with eager work and synchronisation between replays: every replay rewrites
+    o, the checkpoint page and the final page bit-identically to the eager call."""
+    H, D, T = 4, 128, 1000
+    d = G.kda_tokens(77, H, D, 0, T, "bf16")
+    di = inputs_to_dev(d, "bf16")
+    pb = PoolBuf(3, H, D)
+    kw = dict(ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[1], state_out_page=[2])
+    ws = torch.empty(K.kda_prefill_workspace_bytes(pb.pool, T, 1, 1, K.KDA_BF16), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        K.kda_prefill_chunked(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, [0, T],
+                              workspace=ws, **kw)
+
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_pool = o.view(torch.int16).cpu().numpy().copy(), pb.snapshot()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    poison = np.int32(np.uint32(POISON_WORD).view(np.int32))
+    for _ in range(3):
+        o.fill_(float("nan"))
+        pb.buf.fill_(poison)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_pool = pb.snapshot()
+        assert np.array_equal(o.view(torch.int16).cpu().numpy(), ref_o)
+        sw = pb.state_bytes // 4
+        for p in (1, 2):
+            assert np.array_equal(got_pool[p * sw:(p + 1) * sw], ref_pool[p * sw:(p + 1) * sw])
+        assert np.all(got_pool[:sw] == poison)  # page 0 is not an output of the call
