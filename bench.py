@@ -345,6 +345,33 @@ def bench_copy(K, steps, warmup):
             "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_int8(K, steps=20, warmup=10):
+    """int8 compressed checkpoints: quantise 256 active pages (32 heads, d=128)
+    into a compressed pool, and dequantise them back into fp32 pages."""
+    import torch
+    H, D, n = 32, 128, 256
+    sb = H * D * D * 4
+    pool_buf = torch.randn(2 * n * sb // 4, device="cuda") / np.sqrt(D)
+    pool = K.make_pool(pool_buf, sb, 2 * n, H, D)
+    hb = K.kda_ckpt_int8_head_bytes(D, D)
+    qpb = (H * hb + 255) // 256 * 256
+    qbuf = torch.zeros(n * qpb, dtype=torch.uint8, device="cuda")  # touched before timing
+    qpool = K.make_pool(qbuf, qpb, n, H, D)
+    src, dst = list(range(n)), list(range(n, 2 * n))
+    out = {"pages": n, "page_bytes": sb, "compressed_page_bytes": H * hb}
+    for name, fn, kern in (
+            ("write", lambda: K.kda_checkpoint_write_int8(pool, src, qpool, src), "kda_ckpt_quant"),
+            ("restore", lambda: K.kda_checkpoint_restore_int8(qpool, src, pool, dst), "kda_ckpt_dequant")):
+        dev_s, _ = timed(fn, steps, warmup)
+        kt = kernel_times(K, fn, steps)
+        moved = n * (sb + H * hb)  # fp32 page one way, compressed page the other
+        avg = kt[kern]["avg_ms"] / 1e3
+        out[name] = {"ms_per_call": 1e3 * dev_s / steps, "bytes_per_call": moved,
+                     "kernel_avg_ms": 1e3 * avg, "kernel_gbps": moved / avg / 1e9,
+                     "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def cpu_baseline(G, w, d):
     """The fp64 oracle on the same 8K workload (all 32 heads, all tokens), timed on
     this host's cores.  Generation is excluded."""
@@ -430,6 +457,8 @@ def main():
         log(f"decode: {out['decode']}")
         out["checkpoint_copy"] = bench_copy(K, steps=20, warmup=3)
         log(f"copy: {out['checkpoint_copy']}")
+        out["checkpoint_int8"] = bench_int8(K)
+        log(f"int8: {out['checkpoint_int8']}")
         log("varlen resume: 16 sequences")
         out["varlen_resume"] = bench_varlen(K, G)
         log(f"varlen: {out['varlen_resume']}")

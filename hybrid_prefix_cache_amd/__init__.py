@@ -34,7 +34,8 @@ CHUNK = 64
 
 EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset",
            "kda_prefill_workspace_bytes", "kda_prefill_chunked", "kda_decode_step",
-           "kda_checkpoint_write", "kda_checkpoint_restore", "kda_profile_enable",
+           "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
+           "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8", "kda_profile_enable",
            "kda_profile_read")
 
 
@@ -75,6 +76,9 @@ _sig = {
                                        _i32, _P, _P, _P]),
     "kda_checkpoint_write": (ctypes.c_int, [_PP, _P, _P, _i32, _P]),
     "kda_checkpoint_restore": (ctypes.c_int, [_PP, _P, _P, _i32, _P]),
+    "kda_ckpt_int8_head_bytes": (ctypes.c_int64, [_i32, _i32]),
+    "kda_checkpoint_write_int8": (ctypes.c_int, [_PP, _P, _PP, _P, _i32, _P]),
+    "kda_checkpoint_restore_int8": (ctypes.c_int, [_PP, _P, _PP, _P, _i32, _P]),
     "kda_profile_enable": (ctypes.c_int, [_i32]),
     "kda_profile_read": (_i32, [ctypes.POINTER(kda_kernel_stat), _i32, _i32]),
 }
@@ -215,6 +219,23 @@ def kda_checkpoint_write(pool, src_active, dst_ckpt, *, stream=None):
 def kda_checkpoint_restore(pool, src_ckpt, dst_active, *, stream=None):
     s, d = _HostArr(src_ckpt, np.int32), _HostArr(dst_active, np.int32)
     _check(_lib.kda_checkpoint_restore(ctypes.byref(pool), s.ptr, d.ptr, len(s.a), _stream(stream)))
+
+
+def kda_ckpt_int8_head_bytes(d_k: int, d_v: int) -> int:
+    """Bytes of one head in a compressed (int8) checkpoint page; -1 if unsupported."""
+    return int(_lib.kda_ckpt_int8_head_bytes(d_k, d_v))
+
+
+def kda_checkpoint_write_int8(pool, src_active, qpool, dst_qckpt, *, stream=None):
+    s, d = _HostArr(src_active, np.int32), _HostArr(dst_qckpt, np.int32)
+    _check(_lib.kda_checkpoint_write_int8(ctypes.byref(pool), s.ptr, ctypes.byref(qpool), d.ptr,
+                                          len(s.a), _stream(stream)))
+
+
+def kda_checkpoint_restore_int8(qpool, src_qckpt, pool, dst_active, *, stream=None):
+    s, d = _HostArr(src_qckpt, np.int32), _HostArr(dst_active, np.int32)
+    _check(_lib.kda_checkpoint_restore_int8(ctypes.byref(qpool), s.ptr, ctypes.byref(pool), d.ptr,
+                                            len(s.a), _stream(stream)))
 
 
 def kda_profile_enable(on: bool = True):

@@ -411,6 +411,87 @@ kda_status kda_checkpoint_restore(const kda_pool* pool, const int32_t* src_ckpt,
   return copy_pages("kda_checkpoint_restore", pool, src_ckpt, dst_active, n, stream);
 }
 
+// ---- int8 compressed checkpoints ----------------------------------------------
+
+int64_t kda_ckpt_int8_head_bytes(int32_t d_k, int32_t d_v) {
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return -1;
+  return int8_head_bytes(d_k);
+}
+
+static kda_status check_qpool(const char* what, const kda_pool* pool, const kda_pool* qpool) {
+  kda_status s = check_pool(pool);
+  if (s != KDA_OK) return s;
+  if (!qpool) return fail(KDA_ERR_NULL, "%s: qpool descriptor is NULL", what);
+  if (!qpool->base) return fail(KDA_ERR_POOL, "%s: qpool base is NULL", what);
+  if (!aligned(qpool->base, 256)) return fail(KDA_ERR_POOL, "%s: qpool base must be 256-byte aligned", what);
+  if (qpool->num_pages < 1) return fail(KDA_ERR_POOL, "%s: qpool needs num_pages >= 1", what);
+  if (qpool->num_heads != pool->num_heads || qpool->d_k != pool->d_k || qpool->d_v != pool->d_v)
+    return fail(KDA_ERR_SHAPE, "%s: qpool heads/dims (%d, %d, %d) differ from the pool's (%d, %d, %d)",
+                what, qpool->num_heads, qpool->d_k, qpool->d_v, pool->num_heads, pool->d_k, pool->d_v);
+  const int64_t need = (int64_t)qpool->num_heads * int8_head_bytes(qpool->d_k);
+  if (qpool->page_bytes < need || qpool->page_bytes % 256 != 0)
+    return fail(KDA_ERR_POOL, "%s: qpool page_bytes %lld must be a multiple of 256 and >= %lld", what,
+                (long long)qpool->page_bytes, (long long)need);
+  const uintptr_t p0 = reinterpret_cast<uintptr_t>(pool->base);
+  const uintptr_t p1 = p0 + (uintptr_t)pool->num_pages * (uintptr_t)pool->page_bytes;
+  const uintptr_t q0 = reinterpret_cast<uintptr_t>(qpool->base);
+  const uintptr_t q1 = q0 + (uintptr_t)qpool->num_pages * (uintptr_t)qpool->page_bytes;
+  if (p0 < q1 && q0 < p1) return fail(KDA_ERR_PAGE_ALIAS, "%s: pool and qpool byte ranges overlap", what);
+  return KDA_OK;
+}
+
+// src pages index `src_pool`'s range, dst pages `dst_pool`'s.
+static kda_status quant_pages(const char* what, bool to_int8, const kda_pool* pool,
+                              const kda_pool* qpool, const int32_t* src, int32_t src_pages,
+                              const int32_t* dst, int32_t dst_pages, int32_t n, void* stream) {
+  kda_status s = check_qpool(what, pool, qpool);
+  if (s != KDA_OK) return s;
+  if (n < 0) return fail(KDA_ERR_SHAPE, "%s: n < 0", what);
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(KDA_ERR_NULL, "%s: page arrays are NULL", what);
+  std::unordered_set<int32_t> dsts;
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= src_pages || dst[i] < 0 || dst[i] >= dst_pages)
+      return fail(KDA_ERR_PAGE_RANGE, "%s: pair %d (%d -> %d) out of range", what, i, src[i], dst[i]);
+    if (!dsts.insert(dst[i]).second)
+      return fail(KDA_ERR_PAGE_ALIAS, "%s: destination page %d repeats", what, dst[i]);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int32_t b = 0; b < n; b += kCopyPairsPerLaunch) {
+    QuantArgs a;
+    a.pool = static_cast<uint8_t*>(pool->base);
+    a.page_bytes = pool->page_bytes;
+    a.qpool = static_cast<uint8_t*>(qpool->base);
+    a.qpage_bytes = qpool->page_bytes;
+    a.H = pool->num_heads;
+    a.npairs = std::min(kCopyPairsPerLaunch, n - b);
+    for (int32_t i = 0; i < a.npairs; ++i) {
+      a.src[i] = src[b + i];
+      a.dst[i] = dst[b + i];
+    }
+    Launch L(to_int8 ? "kda_ckpt_quant" : "kda_ckpt_dequant", st);
+    hipError_t e = to_int8 ? launch_quant(pool->d_k, a, st) : launch_dequant(pool->d_k, a, st);
+    if (e != hipSuccess) return hip_fail(e, to_int8 ? "quantise launch" : "dequantise launch");
+  }
+  return ok();
+}
+
+kda_status kda_checkpoint_write_int8(const kda_pool* pool, const int32_t* src_active,
+                                     const kda_pool* qpool, const int32_t* dst_qckpt, int32_t n,
+                                     void* stream) {
+  if (!pool || !qpool) return fail(KDA_ERR_NULL, "kda_checkpoint_write_int8: pool descriptor is NULL");
+  return quant_pages("kda_checkpoint_write_int8", true, pool, qpool, src_active, pool->num_pages,
+                     dst_qckpt, qpool->num_pages, n, stream);
+}
+
+kda_status kda_checkpoint_restore_int8(const kda_pool* qpool, const int32_t* src_qckpt,
+                                       const kda_pool* pool, const int32_t* dst_active, int32_t n,
+                                       void* stream) {
+  if (!pool || !qpool) return fail(KDA_ERR_NULL, "kda_checkpoint_restore_int8: pool descriptor is NULL");
+  return quant_pages("kda_checkpoint_restore_int8", false, pool, qpool, src_qckpt, qpool->num_pages,
+                     dst_active, pool->num_pages, n, stream);
+}
+
 kda_status kda_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;

@@ -66,6 +66,23 @@ struct CopyArgs {
   int32_t dst[kCopyPairsPerLaunch];
 };
 static_assert(sizeof(CopyArgs) <= 4096, "kernel argument budget");
+
+// Page pairs of one int8 checkpoint write (src in pool, dst in qpool) or
+// restore (src in qpool, dst in pool) launch.
+struct QuantArgs {
+  uint8_t* pool;
+  int64_t page_bytes;
+  uint8_t* qpool;
+  int64_t qpage_bytes;
+  int32_t H;
+  int32_t npairs;
+  int32_t src[kCopyPairsPerLaunch];
+  int32_t dst[kCopyPairsPerLaunch];
+};
+static_assert(sizeof(QuantArgs) <= 4096, "kernel argument budget");
+
+// Bytes of one head in a compressed page: int8 q[d][d], then fp32 scale[d].
+constexpr int64_t int8_head_bytes(int D) { return (int64_t)D * D + 4LL * D; }
 static_assert(sizeof(MetaFillArgs) <= 4096, "kernel argument budget");
 
 hipError_t launch_meta_fill(const MetaFillArgs& a, hipStream_t st);
@@ -73,5 +90,7 @@ hipError_t launch_prep(int D, bool bf16, const PrepArgs& a, int total_chunks, hi
 hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st);
 hipError_t launch_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t st);
+hipError_t launch_quant(int D, const QuantArgs& a, hipStream_t st);
+hipError_t launch_dequant(int D, const QuantArgs& a, hipStream_t st);
 
 }  // namespace kda

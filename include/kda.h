@@ -25,6 +25,12 @@
  *  [PAGE]  same page, section "La mise en page unifiée": states live in a pool
  *          of pages of one fixed byte size; inside a page the states of all
  *          heads are stored contiguously, head after head.
+ *  [INT8]  "KIMI K3 경량 복제에서 본 KDA의 AI 인프라 과제" (acpost.vercel.app),
+ *          sections 5.3 (Compressed Checkpoint: cached recurrent states may be
+ *          held as int8 with per-channel parameters; a hit dequantises once
+ *          into a fresh active slot and decoding continues at full precision)
+ *          and 6.6.2 (Int8CheckpointStore: one scale per d_k index from the
+ *          max-abs over d_v, symmetric quantisation).
  *
  * Recurrence (decay first, then the delta-rule write, then the read):
  *     S' = Diag(exp(g_t)) S_{t-1};  u = v_t - S'^T k_t;
@@ -197,6 +203,37 @@ kda_status kda_checkpoint_write(const kda_pool* pool, const int32_t* src_active,
  */
 kda_status kda_checkpoint_restore(const kda_pool* pool, const int32_t* src_ckpt,
                                   const int32_t* dst_active, int32_t n, void* stream);
+
+/*
+ * Compressed (int8) checkpoints [INT8].  A compressed page of `qpool` holds,
+ * for each head h at byte offset h * kda_ckpt_int8_head_bytes(d_k, d_v):
+ *     int8_t q[d_k][d_v]   (row i is the d_k index, as in the fp32 state)
+ *     float  scale[d_k]
+ * with, per d_k row i (fp32 arithmetic, IEEE division):
+ *     scale_i = max_j |S_ij| / 127
+ *     q_ij    = clamp(round_half_even(S_ij / scale_i), -127, 127), 0 if scale_i == 0
+ * and restore writes S~_ij = q_ij * scale_i (fp32).  The pages fix neither the
+ * rounding nor the clamp; this is the reading taken.  |S~_ij - S_ij| <=
+ * scale_i / 2.  States must be finite.
+ * qpool: same num_heads, d_k, d_v as pool; page_bytes >= num_heads *
+ * kda_ckpt_int8_head_bytes(d_k, d_v); its byte range must not overlap pool's.
+ * Host index arrays of n entries; pages in range; destinations distinct.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE (pools disagree), KDA_ERR_POOL (qpool
+ * too small / misaligned), KDA_ERR_PAGE_RANGE, KDA_ERR_PAGE_ALIAS (duplicate
+ * destination or overlapping pools), KDA_ERR_HIP.
+ */
+int64_t kda_ckpt_int8_head_bytes(int32_t d_k, int32_t d_v);
+
+/* Quantise active pages pool[src_active[i]] into compressed pages qpool[dst_qckpt[i]]. */
+kda_status kda_checkpoint_write_int8(const kda_pool* pool, const int32_t* src_active,
+                                     const kda_pool* qpool, const int32_t* dst_qckpt, int32_t n,
+                                     void* stream);
+
+/* Dequantise compressed pages qpool[src_qckpt[i]] into fp32 active pages
+ * pool[dst_active[i]] (copy-on-write restore: the compressed page is not modified). */
+kda_status kda_checkpoint_restore_int8(const kda_pool* qpool, const int32_t* src_qckpt,
+                                       const kda_pool* pool, const int32_t* dst_active, int32_t n,
+                                       void* stream);
 
 /*
  * Optional per-kernel timing (tracing aid).  When enabled, every kernel the

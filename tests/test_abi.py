@@ -22,7 +22,7 @@ MiB2 = 2 << 20
 def declared_functions():
     text = open(HDR).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -199,3 +199,53 @@ def test_decode_validation():
 
 def test_version():
     assert K.kda_version() >> 16 >= 1
+
+
+# ---- int8 compressed checkpoints -------------------------------------------
+QFAKE = 1 << 30  # a second fake region, disjoint from the pool's
+QPAGE = 32 * (128 * 128 + 4 * 128)  # 540,672 bytes: 32 heads at d = 128
+
+
+def qpool(**kw):
+    d = dict(base=QFAKE, page_bytes=QPAGE, num_pages=8, num_heads=32, d_k=128)
+    d.update(kw)
+    return K.make_pool(**d)
+
+
+def test_int8_head_bytes():
+    assert K.kda_ckpt_int8_head_bytes(128, 128) == 128 * 128 + 4 * 128
+    assert K.kda_ckpt_int8_head_bytes(64, 64) == 64 * 64 + 4 * 64
+    assert K.kda_ckpt_int8_head_bytes(96, 96) == -1
+    assert K.kda_ckpt_int8_head_bytes(128, 64) == -1
+
+
+@pytest.mark.parametrize("direction", ["write", "restore"])
+@pytest.mark.parametrize("qkw,src,dst,status", [
+    (dict(num_heads=16), [0], [0], K.KDA_ERR_SHAPE),
+    (dict(d_k=64), [0], [0], K.KDA_ERR_SHAPE),
+    (dict(page_bytes=QPAGE - 256), [0], [0], K.KDA_ERR_POOL),
+    (dict(page_bytes=QPAGE + 8), [0], [0], K.KDA_ERR_POOL),
+    (dict(base=0), [0], [0], K.KDA_ERR_POOL),
+    (dict(base=FAKE + 4 * MiB2), [0], [0], K.KDA_ERR_PAGE_ALIAS),  # overlaps the pool
+    (dict(), [0, 1], [2, 2], K.KDA_ERR_PAGE_ALIAS),
+    (dict(), [-1], [0], K.KDA_ERR_PAGE_RANGE),
+])
+def test_int8_validation(direction, qkw, src, dst, status):
+    with pytest.raises(K.KdaError) as ei:
+        if direction == "write":
+            K.kda_checkpoint_write_int8(pool(), src, qpool(**qkw), dst, stream=0)
+        else:
+            K.kda_checkpoint_restore_int8(qpool(**qkw), src, pool(), dst, stream=0)
+    assert ei.value.status == status
+
+
+def test_int8_page_ranges_follow_direction():
+    # write: sources index the pool (16 pages), destinations the qpool (8 pages)
+    with pytest.raises(K.KdaError) as ei:
+        K.kda_checkpoint_write_int8(pool(), [15], qpool(), [8], stream=0)
+    assert ei.value.status == K.KDA_ERR_PAGE_RANGE
+    # restore: sources index the qpool, destinations the pool
+    with pytest.raises(K.KdaError) as ei:
+        K.kda_checkpoint_restore_int8(qpool(), [8], pool(), [15], stream=0)
+    assert ei.value.status == K.KDA_ERR_PAGE_RANGE
+    K.kda_checkpoint_write_int8(pool(), [], qpool(), [], stream=0)  # empty: nothing enqueued
