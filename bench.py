@@ -48,13 +48,15 @@ SCAN_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2
 # HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs over this
 # script, summarised by --summarize-pmc; valid only while the kernel source
 # still hashes to the value recorded with the counters.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_prefill8k_decode256_copy256.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_prefill8k_decode256_copy256_int8x256.md")
 KERNEL_SOURCES = {"kda_prefill_prep": "kda_prefill.hip", "kda_prefill_scan": "kda_prefill.hip",
-                  "kda_decode_step": "kda_decode.hip", "kda_page_copy": "kda_copy.hip"}
+                  "kda_decode_step": "kda_decode.hip", "kda_page_copy": "kda_copy.hip",
+                  "kda_ckpt_quant": "kda_ckpt_int8.hip", "kda_ckpt_dequant": "kda_ckpt_int8.hip"}
 # device kernel symbol -> library launch name
 KERNEL_SYMBOLS = {"prep2_kernel": "kda_prefill_prep", "prep_kernel": "kda_prefill_prep",
                   "scan_kernel": "kda_prefill_scan", "decode_kernel": "kda_decode_step",
-                  "copy_kernel": "kda_page_copy", "meta_fill_kernel": "kda_meta_fill"}
+                  "copy_kernel": "kda_page_copy", "meta_fill_kernel": "kda_meta_fill",
+                  "quant_kernel": "kda_ckpt_quant", "dequant_kernel": "kda_ckpt_dequant"}
 
 
 def log(*a):
@@ -105,7 +107,8 @@ def summarize_pmc(fetch_dir, write_dir, command):
     lines = [
         "# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
         "Workloads: prefill 8K x 32 heads x d=128 bf16 with 3 checkpoints; decode 256 requests x",
-        "32 heads; page copy 256 x 2 MiB.  Commands (from /tmp, TMPDIR=/tmp, R = repository root):", "",
+        "32 heads; page copy 256 x 2 MiB; int8 checkpoint write / restore of 256 pages.  Commands",
+        "(from /tmp, TMPDIR=/tmp, R = repository root):", "",
         "```", *command, "```", "",
         f"Calibration against the page copy (512 MiB read + 512 MiB written per launch): "
         f"FETCH_SIZE x {kf:.3f}, WRITE_SIZE x {kw:.3f}.  Source hash = first 16 hex digits of the",
@@ -394,12 +397,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only-prefill", action="store_true")
+    ap.add_argument("--only-core", action="store_true",
+                    help="skip the resume and 2^20-token workloads (profiling runs: one prefill shape)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the markdown traffic summary of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
     if args.summarize_pmc:
         cmd = [f"rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{d} -o run -- "
-               f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu"
+               f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu --only-core"
                for c, d in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write"))]
         cmd.append("python3 $R/bench.py --summarize-pmc $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write")
         sys.stdout.write(summarize_pmc(*args.summarize_pmc, cmd))
@@ -459,6 +464,7 @@ def main():
         log(f"copy: {out['checkpoint_copy']}")
         out["checkpoint_int8"] = bench_int8(K)
         log(f"int8: {out['checkpoint_int8']}")
+    if not args.only_prefill and not args.only_core:
         log("varlen resume: 16 sequences")
         out["varlen_resume"] = bench_varlen(K, G)
         log(f"varlen: {out['varlen_resume']}")
