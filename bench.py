@@ -348,6 +348,33 @@ def bench_copy(K, steps, warmup):
             "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_verify(K, G, steps=20, warmup=5, n=128, ntok=4):
+    """Speculative verification: 4 draft tokens for each of 128 requests x 32
+    heads in one launch, every intermediate state written to its own page."""
+    import torch
+    H, D = 32, 128
+    sb = H * D * D * 4
+    pool_buf = torch.randn((n + n * ntok) * sb // 4, device="cuda") / np.sqrt(D)
+    pool = K.make_pool(pool_buf, sb, n + n * ntok, H, D)
+    d = G.kda_tokens(0x4B44416, H, D, 0, n * ntok, "bf16")
+    di = {k: to_dev(v, "bf16") for k, v in d.items()}
+    o = torch.empty((n * ntok, H, D), dtype=torch.bfloat16, device="cuda")
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    pout = torch.arange(n, n + n * ntok, dtype=torch.int32, device="cuda")
+
+    def step():
+        K.kda_decode_verify(pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, ntok, pin, pout)
+
+    dev_s, _ = timed(step, steps, warmup)
+    kt = kernel_times(K, step, steps)
+    moved = n * H * (D * D * 4 * (1 + ntok) + ntok * (4 * D * 2 + 2 + D * 2))
+    avg = kt["kda_decode_verify"]["avg_ms"] / 1e3
+    return {"requests": n, "tokens_per_request": ntok, "bytes_per_call": moved,
+            "ms_per_call": 1e3 * dev_s / steps, "kernel_avg_ms": 1e3 * avg,
+            "kernel_gbps": moved / avg / 1e9, "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": n * ntok * steps / dev_s}
+
+
 def bench_int8(K, steps=20, warmup=10):
     """int8 compressed checkpoints: quantise 256 active pages (32 heads, d=128)
     into a compressed pool, and dequantise them back into fp32 pages."""
@@ -464,6 +491,8 @@ def main():
         log(f"copy: {out['checkpoint_copy']}")
         out["checkpoint_int8"] = bench_int8(K)
         log(f"int8: {out['checkpoint_int8']}")
+        out["verify"] = bench_verify(K, G)
+        log(f"verify: {out['verify']}")
     if not args.only_prefill and not args.only_core:
         log("varlen resume: 16 sequences")
         out["varlen_resume"] = bench_varlen(K, G)

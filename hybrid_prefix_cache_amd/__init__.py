@@ -34,6 +34,7 @@ CHUNK = 64
 
 EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset",
            "kda_prefill_workspace_bytes", "kda_prefill_chunked", "kda_decode_step",
+           "kda_decode_verify",
            "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
            "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8", "kda_profile_enable",
            "kda_profile_read")
@@ -58,7 +59,7 @@ class kda_kernel_stat(ctypes.Structure):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libkda.so is not built ({LIB_PATH}); run "
-                      "`python -m hybrid_prefix_cache_amd.build` (hipcc, gfx950)")
+                      "`python hybrid_prefix_cache_amd/build.py` (hipcc, gfx950)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -74,6 +75,8 @@ _sig = {
                                            _P]),
     "kda_decode_step": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
                                        _i32, _P, _P, _P]),
+    "kda_decode_verify": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
+                                         _i32, _i32, _P, _P, _P]),
     "kda_checkpoint_write": (ctypes.c_int, [_PP, _P, _P, _i32, _P]),
     "kda_checkpoint_restore": (ctypes.c_int, [_PP, _P, _P, _i32, _P]),
     "kda_ckpt_int8_head_bytes": (ctypes.c_int64, [_i32, _i32]),
@@ -208,6 +211,20 @@ def kda_decode_step(pool, q, k, v, g, beta, o, page_in, page_out, *, n=None, in_
     st = _lib.kda_decode_step(ctypes.byref(pool), _dptr(q), _dptr(k), _dptr(v), _dptr(g),
                               _dptr(beta), ind, _dptr(o), outd, n, _dptr(page_in),
                               _dptr(page_out), _stream(stream))
+    _check(st)
+
+
+def kda_decode_verify(pool, q, k, v, g, beta, o, tokens, page_in, page_out, *, n=None,
+                      in_dtype=None, out_dtype=None, stream=None):
+    """`tokens` consecutive tokens per request, every intermediate state kept.
+    q, k, g: [n*tokens, H, d_k]; v, o: [n*tokens, H, d_v]; beta: [n*tokens, H];
+    page_in: int32 device [n]; page_out: int32 device [n*tokens]."""
+    n = int(page_in.numel()) if n is None else n
+    ind = _dtype_code(q) if in_dtype is None else in_dtype
+    outd = _dtype_code(o) if out_dtype is None else out_dtype
+    st = _lib.kda_decode_verify(ctypes.byref(pool), _dptr(q), _dptr(k), _dptr(v), _dptr(g),
+                                _dptr(beta), ind, _dptr(o), outd, n, int(tokens), _dptr(page_in),
+                                _dptr(page_out), _stream(stream))
     _check(st)
 
 

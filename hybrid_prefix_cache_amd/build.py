@@ -1,6 +1,7 @@
 """Build libkda.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: python -m hybrid_prefix_cache_amd.build
+Usage: python hybrid_prefix_cache_amd/build.py   (run as a file: importing the
+package first would bind the symbols of a possibly stale libkda.so)
 """
 from __future__ import annotations
 

@@ -323,44 +323,70 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
   return ok();
 }
 
+static kda_status decode_impl(const char* what, const kda_pool* pool, const void* q, const void* k,
+                              const void* v, const void* g, const void* beta, kda_dtype in_dtype,
+                              void* o, kda_dtype out_dtype, int32_t n, int32_t K,
+                              const int32_t* page_in, const int32_t* page_out, void* stream) {
+  kda_status s = check_pool(pool);
+  if (s != KDA_OK) return s;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(KDA_ERR_DTYPE, "%s: unknown dtype code (in %d, out %d)", what, (int)in_dtype,
+                (int)out_dtype);
+  if (n < 0) return fail(KDA_ERR_SHAPE, "%s: n < 0", what);
+  if (K < 1 || K > kMaxVerifyTokens)
+    return fail(KDA_ERR_SHAPE, "%s: tokens per request %d outside [1, %d]", what, K, kMaxVerifyTokens);
+  if (n == 0) return ok();
+  if (!q || !k || !v || !g || !beta || !o || !page_in || !page_out)
+    return fail(KDA_ERR_NULL, "%s: q, k, v, g, beta, o, page_in and page_out must be non-NULL", what);
+  if ((int64_t)n * K * pool->num_heads > (int64_t)1 << 30)
+    return fail(KDA_ERR_SHAPE, "%s: n * K * H too large", what);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const char* val = std::getenv("KDA_VALIDATE");
+  if (val && val[0] == '1') {
+    const int64_t nout = (int64_t)n * K;
+    std::vector<int32_t> pin(n), pout(nout);
+    hipError_t e = hipMemcpyAsync(pin.data(), page_in, n * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(pout.data(), page_out, nout * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "page table read-back");
+    std::unordered_set<int32_t> outs;
+    for (int32_t r = 0; r < n; ++r)
+      if (pin[r] < 0 || pin[r] >= pool->num_pages)
+        return fail(KDA_ERR_PAGE_RANGE, "%s: request %d: page_in %d out of range", what, r, pin[r]);
+    for (int64_t i = 0; i < nout; ++i) {
+      if (pout[i] < 0 || pout[i] >= pool->num_pages)
+        return fail(KDA_ERR_PAGE_RANGE, "%s: page_out[%lld] = %d out of range", what, (long long)i, pout[i]);
+      if (!outs.insert(pout[i]).second)
+        return fail(KDA_ERR_PAGE_ALIAS, "%s: page_out %d repeats", what, pout[i]);
+    }
+    for (int32_t r = 0; r < n; ++r)
+      for (int64_t i = 0; i < nout; ++i)
+        if (pout[i] == pin[r] && i / K != r)
+          return fail(KDA_ERR_PAGE_ALIAS, "%s: page_in[%d] = %d is another request's output", what, r,
+                      pin[r]);
+  }
+  DecodeArgs a{q, k, v, g, beta, o, page_in, page_out, static_cast<uint8_t*>(pool->base),
+               pool->page_bytes, pool->num_pages, pool->num_heads, out_dtype == KDA_BF16, n, K};
+  Launch L(K == 1 ? "kda_decode_step" : "kda_decode_verify", st);
+  hipError_t e = launch_decode(pool->d_k, in_dtype == KDA_BF16, a, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
 kda_status kda_decode_step(const kda_pool* pool, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, kda_dtype in_dtype, void* o,
                            kda_dtype out_dtype, int32_t n, const int32_t* page_in,
                            const int32_t* page_out, void* stream) {
-  kda_status s = check_pool(pool);
-  if (s != KDA_OK) return s;
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
-    return fail(KDA_ERR_DTYPE, "unknown dtype code (in %d, out %d)", (int)in_dtype, (int)out_dtype);
-  if (n < 0) return fail(KDA_ERR_SHAPE, "n < 0");
-  if (n == 0) return ok();
-  if (!q || !k || !v || !g || !beta || !o || !page_in || !page_out)
-    return fail(KDA_ERR_NULL, "q, k, v, g, beta, o, page_in and page_out must be non-NULL");
-  if ((int64_t)n * pool->num_heads > (int64_t)1 << 30) return fail(KDA_ERR_SHAPE, "n * H too large");
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const char* val = std::getenv("KDA_VALIDATE");
-  if (val && val[0] == '1') {
-    std::vector<int32_t> pin(n), pout(n);
-    hipError_t e = hipMemcpyAsync(pin.data(), page_in, n * 4, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipMemcpyAsync(pout.data(), page_out, n * 4, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "page table read-back");
-    std::unordered_set<int32_t> outs;
-    for (int32_t r = 0; r < n; ++r) {
-      if (pin[r] < 0 || pin[r] >= pool->num_pages || pout[r] < 0 || pout[r] >= pool->num_pages)
-        return fail(KDA_ERR_PAGE_RANGE, "request %d: pages %d -> %d", r, pin[r], pout[r]);
-      if (!outs.insert(pout[r]).second)
-        return fail(KDA_ERR_PAGE_ALIAS, "page_out %d repeats", pout[r]);
-    }
-    for (int32_t r = 0; r < n; ++r)
-      if (outs.count(pin[r]) && pout[r] != pin[r])
-        return fail(KDA_ERR_PAGE_ALIAS, "page_in[%d] = %d is another request's output", r, pin[r]);
-  }
-  DecodeArgs a{q, k, v, g, beta, o, page_in, page_out, static_cast<uint8_t*>(pool->base),
-               pool->page_bytes, pool->num_pages, pool->num_heads, out_dtype == KDA_BF16, n};
-  Launch L("kda_decode_step", st);
-  hipError_t e = launch_decode(pool->d_k, in_dtype == KDA_BF16, a, st);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return ok();
+  return decode_impl("kda_decode_step", pool, q, k, v, g, beta, in_dtype, o, out_dtype, n, 1, page_in,
+                     page_out, stream);
+}
+
+kda_status kda_decode_verify(const kda_pool* pool, const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                             kda_dtype out_dtype, int32_t n, int32_t tokens, const int32_t* page_in,
+                             const int32_t* page_out, void* stream) {
+  return decode_impl("kda_decode_verify", pool, q, k, v, g, beta, in_dtype, o, out_dtype, n, tokens,
+                     page_in, page_out, stream);
 }
 
 static kda_status copy_pages(const char* what, const kda_pool* pool, const int32_t* src,

@@ -21,6 +21,14 @@
 // holding 16 rows per thread with ordinary loads.  The two column sums over
 // rows (S'^T k and S^T q) use lane shuffles inside a wave, then one LDS
 // exchange across the waves.
+//
+// The same kernel applies K tokens per request in one launch (speculative
+// verification, page "KIMI K3 경량 복제에서 본 KDA의 AI 인프라 과제", sections
+// 6.4/6.5: a target-verify path keeps every intermediate state, indexed per
+// token, so that rejected draft tokens roll back): the state stays in registers from token to token
+// and the state after token t is written to page_out[r*K + t]; a plain
+// decode step is K = 1.  The reduction scratch alternates between two buffers
+// by token parity, so consecutive tokens need no extra barrier.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -41,24 +49,26 @@ template <int D, typename In>
 __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArgs a) {
   using SH = DecodeShape<D>;
   constexpr int VPT = SH::VPT, NQ = SH::NQ, NW = SH::NW, RS = SH::RS;
-  __shared__ f32x4 red[NW][NQ];
-  __shared__ f32x4 sh_u[NQ];
+  __shared__ f32x4 red[2][NW][NQ];
+  __shared__ f32x4 sh_u[2][NQ];
 
   const int r = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int cq = tid % NQ, rg = tid / NQ, c0 = 4 * cq;
-  const int64_t row = (int64_t)r * a.H + h;  // (request, head) input row
-  const In* gq = reinterpret_cast<const In*>(a.q) + row * D;
-  const In* gk = reinterpret_cast<const In*>(a.k) + row * D;
-  const In* gv = reinterpret_cast<const In*>(a.v) + row * D;
-  const In* gg = reinterpret_cast<const In*>(a.g) + row * D;
-  const int pin = a.page_in[r], pout = a.page_out[r];
-  const bool ok = pin >= 0 && pin < a.num_pages && pout >= 0 && pout < a.num_pages;
-  if (!ok) {  // bad page index: touch no state, make the output loudly wrong
-    if (tid < D) {
-      const int64_t oi = row * D + tid;
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = 0x7fc0u;
-      else reinterpret_cast<float*>(a.o)[oi] = __builtin_nanf("");
+  const int K = a.K;
+  const int pin = a.page_in[r];
+  bool ok = pin >= 0 && pin < a.num_pages;
+  for (int t = 0; t < K; ++t) {
+    const int po = a.page_out[r * K + t];
+    ok = ok && po >= 0 && po < a.num_pages;
+  }
+  if (!ok) {  // a bad page index: touch no state, make this request's outputs loudly wrong
+    for (int t = 0; t < K; ++t) {
+      if (tid < D) {
+        const int64_t oi = ((int64_t)(r * K + t) * a.H + h) * D + tid;
+        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.o)[oi] = 0x7fc0u;
+        else reinterpret_cast<float*>(a.o)[oi] = __builtin_nanf("");
+      }
     }
     return;
   }
@@ -68,17 +78,6 @@ __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArg
 #pragma unroll
   for (int i = 0; i < VPT; ++i)
     s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (rg + i * RS) * D + c0));
-  float kr[VPT], qr[VPT];
-  f32x4 p = zero4();
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {  // S' = diag(alpha) S ; partial S'^T k over this thread's rows
-    const int c = rg + i * RS;
-    const float ac = __expf(in_f(gg[c]));
-    kr[i] = in_f(gk[c]);
-    qr[i] = in_f(gq[c]);
-    s[i] *= ac;
-    p += s[i] * kr[i];
-  }
   // sum over the row groups inside a wave: lanes that differ above the column-quad bits
   auto wave_sum = [&](f32x4 x) {
 #pragma unroll
@@ -88,40 +87,59 @@ __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArg
     }
     return x;
   };
-  p = wave_sum(p);
-  if (lane < NQ) red[wv][cq] = p;
-  __syncthreads();
-  if (tid < NQ) {
-    f32x4 acc = red[0][tid];
+  for (int t = 0; t < K; ++t) {
+    const int par = t & 1;
+    const int64_t row = (int64_t)(r * K + t) * a.H + h;  // (token, head) input row
+    const In* gq = reinterpret_cast<const In*>(a.q) + row * D;
+    const In* gk = reinterpret_cast<const In*>(a.k) + row * D;
+    const In* gv = reinterpret_cast<const In*>(a.v) + row * D;
+    const In* gg = reinterpret_cast<const In*>(a.g) + row * D;
+    float kr[VPT], qr[VPT];
+    f32x4 p = zero4();
 #pragma unroll
-    for (int w = 1; w < NW; ++w) acc += red[w][tid];
-    const int c = 4 * tid;
-    sh_u[tid] = f32x4{in_f(gv[c]) - acc.x, in_f(gv[c + 1]) - acc.y, in_f(gv[c + 2]) - acc.z,
-                      in_f(gv[c + 3]) - acc.w};  // u = v - S'^T k
-  }
-  __syncthreads();
-  const f32x4 u = sh_u[cq];
-  const float beta = in_f(reinterpret_cast<const In*>(a.beta)[row]);
-  float* dst = reinterpret_cast<float*>(a.pool + pout * a.page_bytes) + hoff;
-  f32x4 po = zero4();
+    for (int i = 0; i < VPT; ++i) {  // S' = diag(alpha) S ; partial S'^T k over this thread's rows
+      const int c = rg + i * RS;
+      const float ac = __expf(in_f(gg[c]));
+      kr[i] = in_f(gk[c]);
+      qr[i] = in_f(gq[c]);
+      s[i] *= ac;
+      p += s[i] * kr[i];
+    }
+    p = wave_sum(p);
+    if (lane < NQ) red[par][wv][cq] = p;
+    __syncthreads();
+    if (tid < NQ) {
+      f32x4 acc = red[par][0][tid];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {  // S = S' + beta k u^T ; partial S^T q
-    s[i] += u * (beta * kr[i]);
-    __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(dst + (rg + i * RS) * D + c0));
-    po += s[i] * qr[i];
-  }
-  po = wave_sum(po);
-  if (lane < NQ) red[wv][cq] = po;  // the first sum's reads finished before the last barrier
-  __syncthreads();
-  if (tid < NQ) {
-    f32x4 acc = red[0][tid];
+      for (int w = 1; w < NW; ++w) acc += red[par][w][tid];
+      const int c = 4 * tid;
+      sh_u[par][tid] = f32x4{in_f(gv[c]) - acc.x, in_f(gv[c + 1]) - acc.y, in_f(gv[c + 2]) - acc.z,
+                             in_f(gv[c + 3]) - acc.w};  // u = v - S'^T k
+    }
+    __syncthreads();
+    const f32x4 u = sh_u[par][cq];
+    const float beta = in_f(reinterpret_cast<const In*>(a.beta)[row]);
+    float* dst = reinterpret_cast<float*>(a.pool + a.page_out[r * K + t] * a.page_bytes) + hoff;
+    f32x4 pq = zero4();
 #pragma unroll
-    for (int w = 1; w < NW; ++w) acc += red[w][tid];
-    const int64_t oi = row * D + 4 * tid;
-    if (a.out_bf16)
-      *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + oi) = pack_bf16x4(acc.x, acc.y, acc.z, acc.w);
-    else
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + oi) = acc;
+    for (int i = 0; i < VPT; ++i) {  // S = S' + beta k u^T ; partial S^T q
+      s[i] += u * (beta * kr[i]);
+      __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(dst + (rg + i * RS) * D + c0));
+      pq += s[i] * qr[i];
+    }
+    pq = wave_sum(pq);
+    if (lane < NQ) red[par][wv][cq] = pq;  // this buffer's first sum was read before the last barrier
+    __syncthreads();
+    if (tid < NQ) {
+      f32x4 acc = red[par][0][tid];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) acc += red[par][w][tid];
+      const int64_t oi = row * D + 4 * tid;
+      if (a.out_bf16)
+        *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(a.o) + oi) = pack_bf16x4(acc.x, acc.y, acc.z, acc.w);
+      else
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + oi) = acc;
+    }
   }
 }
 

@@ -36,6 +36,8 @@ struct ScanArgs {
   int64_t page_bytes;
 };
 
+constexpr int kMaxVerifyTokens = 64;  // tokens per request in one decode launch
+
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -50,7 +52,8 @@ struct DecodeArgs {
   int32_t num_pages;
   int32_t H;
   int32_t out_bf16;
-  int32_t n;
+  int32_t n;   // requests
+  int32_t K;   // tokens per request: rows r*K + t, state after token t -> page_out[r*K + t]
 };
 
 constexpr int kCopyPairsPerLaunch = 448;

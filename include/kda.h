@@ -189,6 +189,33 @@ kda_status kda_decode_step(const kda_pool* pool, const void* q, const void* k, c
                            const int32_t* page_out, void* stream);
 
 /*
+ * Speculative verification [ARCH][AFF 2.1]: apply `tokens` (1..64) consecutive
+ * tokens to each of n requests in one launch, keeping every intermediate
+ * state so that rejected draft tokens can be rolled back (page "KIMI K3 경량
+ * 복제에서 본 KDA의 AI 인프라 과제", sections 6.4 and 6.5: the kernel
+ * dispatcher has a target-verify path next to decode and prefill, and one KDA
+ * run carries the recurrent state together with the indices of the verify
+ * step's intermediate states).  Token t of request r is input row r*tokens + t:
+ *   q, k, g : [n*tokens, H, d_k]; v : [n*tokens, H, d_v]; beta : [n*tokens, H]
+ *   o       : [n*tokens, H, d_v]
+ *   page_in : [n] int32 DEVICE array, the state before the first token;
+ *   page_out: [n*tokens] int32 DEVICE array, page_out[r*tokens + t] receives the
+ *             state after token t (so accepting a tokens of request r means
+ *             continuing from page_out[r*tokens + a - 1]).
+ * The state is read once and stays on chip from token to token; outputs equal
+ * those of `tokens` consecutive kda_decode_step calls bit for bit.  page_out
+ * entries must be distinct and none may equal another request's page_in (one
+ * of a request's own outputs may equal its page_in).  Device-side: a request
+ * with any page index outside [0, num_pages) touches no state and gets NaN
+ * outputs for all its tokens; KDA_VALIDATE=1 checks the tables on the host.
+ * kda_decode_step is the case tokens = 1.
+ */
+kda_status kda_decode_verify(const kda_pool* pool, const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                             kda_dtype out_dtype, int32_t n, int32_t tokens, const int32_t* page_in,
+                             const int32_t* page_out, void* stream);
+
+/*
  * Checkpoint write [CKPT]: copy the state bytes (num_heads * d_k * d_v * 4) of
  * page src_active[i] to page dst_ckpt[i], i < n.  Host index arrays.  Pages in
  * range; destinations distinct and never a source of the same call.

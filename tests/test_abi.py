@@ -249,3 +249,15 @@ def test_int8_page_ranges_follow_direction():
         K.kda_checkpoint_restore_int8(qpool(), [8], pool(), [15], stream=0)
     assert ei.value.status == K.KDA_ERR_PAGE_RANGE
     K.kda_checkpoint_write_int8(pool(), [], qpool(), [], stream=0)  # empty: nothing enqueued
+
+
+def test_verify_validation():
+    p = pool()
+    call = lambda n, tok, pin=FAKE, pout=FAKE: K.raw_call(  # noqa: E731
+        "kda_decode_verify", ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, K.KDA_BF16, FAKE,
+        K.KDA_BF16, n, tok, pin, pout, None)
+    assert call(4, 0) == K.KDA_ERR_SHAPE
+    assert call(4, 65) == K.KDA_ERR_SHAPE
+    assert call(-1, 2) == K.KDA_ERR_SHAPE
+    assert call(4, 2, pout=None) == K.KDA_ERR_NULL
+    assert call(0, 2, None, None) == K.KDA_OK  # no requests: nothing to do

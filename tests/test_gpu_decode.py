@@ -133,3 +133,96 @@ def test_decode_deterministic():
         torch.cuda.synchronize()
         outs.append((o.view(torch.int16).cpu().numpy(), pb.snapshot()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ---- speculative verification: tokens per request in one launch ------------
+
+def _verify_setup(n, H, D, ntok, dtype, seed):
+    s0 = G.random_states(seed, n, H, D)
+    d = G.kda_tokens(seed, H, D, 0, n * ntok, dtype)  # row r*ntok + t = token t of request r
+    return s0, d
+
+
+def test_verify_equals_sequential_steps_bitwise():
+    """tokens = 4 in one launch == 4 kda_decode_step calls, bit for bit, on o
+    and on every intermediate state."""
+    n, H, D, ntok = 8, 4, 128, 4
+    s0, d = _verify_setup(n, H, D, ntok, "bf16", 31)
+    di = {k: dev(v, "bf16") for k, v in d.items()}
+    pb = PoolBuf(n * (ntok + 1) * 2, H, D)
+    base = n * (ntok + 1)
+    for r in range(n):
+        pb.set_states(r, s0[r])
+        pb.set_states(base + r, s0[r])
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    pout = torch.arange(n, n + n * ntok, dtype=torch.int32, device="cuda")  # r*ntok + t -> page n + r*ntok + t
+    o_v = torch.empty((n * ntok, H, D), dtype=torch.bfloat16, device="cuda")
+    K.kda_decode_verify(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o_v, ntok, pin, pout)
+    # sequential: step t reads the page written by step t-1
+    o_s = torch.empty((n * ntok, H, D), dtype=torch.bfloat16, device="cuda")
+    rows = torch.arange(n, device="cuda") * ntok
+    cur = torch.arange(base, base + n, dtype=torch.int32, device="cuda")
+    for t in range(ntok):
+        nxt = (base + n + rows + t).to(torch.int32)
+        sel = rows + t
+        o_t = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+        K.kda_decode_step(pb.pool, di["q"][sel], di["k"][sel], di["v"][sel], di["g"][sel],
+                          di["beta"][sel], o_t, cur, nxt)
+        o_s[sel] = o_t
+        cur = nxt
+    torch.cuda.synchronize()
+    assert torch.equal(o_v.view(torch.int16), o_s.view(torch.int16))
+    for r in range(n):
+        for t in range(ntok):
+            assert np.array_equal(pb.states(n + r * ntok + t), pb.states(base + n + r * ntok + t)), (r, t)
+
+
+@pytest.mark.parametrize("dtype,D,ntok", [("bf16", 128, 6), ("f32", 64, 5)])
+def test_verify_oracle(dtype, D, ntok):
+    """Each request's ntok tokens against the oracle run over them with a
+    checkpoint after every token."""
+    n, H = 4, 3
+    s0, d = _verify_setup(n, H, D, ntok, dtype, 41 + D)
+    di = {k: dev(v, dtype) for k, v in d.items()}
+    pb = PoolBuf(n + n * ntok, H, D)
+    for r in range(n):
+        pb.set_states(r, s0[r])
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    pout = torch.arange(n, n + n * ntok, dtype=torch.int32, device="cuda")
+    o = torch.empty((n * ntok, H, D), dtype=tdtype(dtype), device="cuda")
+    K.kda_decode_verify(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, ntok, pin, pout)
+    torch.cuda.synchronize()
+    cu = [ntok * r for r in range(n + 1)]
+    ref = oracle.run(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, s0=s0.astype(np.float64),
+                     ckpt_cu=[ntok * r for r in range(n + 1)], ckpt_pos=[t + 1 for _ in range(n) for t in range(ntok)])
+    got = o.double().cpu().numpy()
+    worst = 0.0
+    for r in range(n):
+        for h in range(H):
+            worst = max(worst, rel_fro(got[r * ntok:(r + 1) * ntok, h], ref["o"][r * ntok:(r + 1) * ntok, h]))
+            for t in range(ntok):
+                worst = max(worst, rel_fro(pb.states(n + r * ntok + t)[h], ref["ckpts"][r * ntok + t, h]))
+    assert worst <= TOL[dtype], worst
+
+
+def test_verify_bad_page_is_loud_and_harmless():
+    n, H, D, ntok = 3, 2, 64, 3
+    s0, d = _verify_setup(n, H, D, ntok, "bf16", 7)
+    di = {k: dev(v, "bf16") for k, v in d.items()}
+    pb = PoolBuf(n + n * ntok, H, D)
+    for r in range(n):
+        pb.set_states(r, s0[r])
+    before = pb.snapshot()
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    po = list(range(n, n + n * ntok))
+    po[1 * ntok + 2] = 10 ** 6  # request 1's last page index is out of range
+    pout = torch.tensor(po, dtype=torch.int32, device="cuda")
+    o = torch.zeros((n * ntok, H, D), dtype=torch.bfloat16, device="cuda")
+    K.kda_decode_verify(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, ntok, pin, pout)
+    torch.cuda.synchronize()
+    of = o.float().cpu().numpy()
+    assert np.all(np.isnan(of[ntok:2 * ntok])) and not np.any(np.isnan(of[:ntok])) and not np.any(np.isnan(of[2 * ntok:]))
+    after = pb.snapshot()
+    w = pb.page_bytes // 4
+    for p in range(n + ntok, n + 2 * ntok - 1):  # request 1's valid output pages stay untouched
+        assert np.array_equal(before[p * w:(p + 1) * w], after[p * w:(p + 1) * w])
