@@ -51,12 +51,14 @@ SCAN_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_prefill8k_decode256_copy256_int8x256.md")
 KERNEL_SOURCES = {"kda_prefill_prep": "kda_prefill.hip", "kda_prefill_scan": "kda_prefill.hip",
                   "kda_decode_step": "kda_decode.hip", "kda_page_copy": "kda_copy.hip",
-                  "kda_ckpt_quant": "kda_ckpt_int8.hip", "kda_ckpt_dequant": "kda_ckpt_int8.hip"}
+                  "kda_ckpt_quant": "kda_ckpt_int8.hip", "kda_ckpt_dequant": "kda_ckpt_int8.hip",
+                  "kda_short_conv": "kda_conv.hip"}
 # device kernel symbol -> library launch name
 KERNEL_SYMBOLS = {"prep2_kernel": "kda_prefill_prep", "prep_kernel": "kda_prefill_prep",
                   "scan_kernel": "kda_prefill_scan", "decode_kernel": "kda_decode_step",
                   "copy_kernel": "kda_page_copy", "meta_fill_kernel": "kda_meta_fill",
-                  "quant_kernel": "kda_ckpt_quant", "dequant_kernel": "kda_ckpt_dequant"}
+                  "quant_kernel": "kda_ckpt_quant", "dequant_kernel": "kda_ckpt_dequant",
+                  "conv_kernel": "kda_short_conv"}
 
 
 def log(*a):
@@ -402,6 +404,35 @@ def bench_int8(K, steps=20, warmup=10):
     return out
 
 
+def bench_conv(K, G, steps=20, warmup=5, T=8192, C=3 * 32 * 128, W=4):
+    """Short causal convolution (width 4) over the fused q|k|v projection of
+    the 8192-token prefill (3 x 32 heads x 128 channels per token, bf16, one
+    call), with the window checkpointed at every 512-token boundary and a
+    final window page."""
+    import torch
+    x = to_dev(G.conv_inputs(11, T, C, "bf16"), "bf16")
+    wt = torch.from_numpy(G.conv_weights(11, C, W)).cuda()
+    y = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    P = list(range(512, T + 1, 512))
+    win = (W - 1) * C * 2
+    pb = (win + 255) // 256 * 256
+    cbuf = torch.zeros((len(P) + 1) * pb, dtype=torch.uint8, device="cuda")
+    cpool = K.make_conv_pool(cbuf, pb, len(P) + 1, C, W, K.KDA_BF16)
+    wsb = torch.empty(K.kda_conv_workspace_bytes(1, len(P)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        K.kda_short_conv(cpool, x, wt, y, [0, T], state_out_page=[0], ckpt_cu=[0, len(P)],
+                         ckpt_pos=P, ckpt_page=list(range(1, 1 + len(P))), workspace=wsb)
+    dev_s, _ = timed(step, steps, warmup)
+    kt = kernel_times(K, step, steps)
+    moved = 2 * T * C * 2 + (len(P) + 1) * win + C * W * 4  # x in, y out, windows, taps
+    avg = kt["kda_short_conv"]["avg_ms"] / 1e3
+    return {"T": T, "channels": C, "width": W, "checkpoints": len(P),
+            "ms_per_call": 1e3 * dev_s / steps, "bytes_per_call": moved,
+            "kernel_avg_ms": 1e3 * avg, "kernel_gbps": moved / avg / 1e9,
+            "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(G, w, d):
     """The fp64 oracle on the same 8K workload (all 32 heads, all tokens), timed on
     this host's cores.  Generation is excluded."""
@@ -493,6 +524,8 @@ def main():
         log(f"int8: {out['checkpoint_int8']}")
         out["verify"] = bench_verify(K, G)
         log(f"verify: {out['verify']}")
+        out["short_conv"] = bench_conv(K, G)
+        log(f"conv: {out['short_conv']}")
     if not args.only_prefill and not args.only_core:
         log("varlen resume: 16 sequences")
         out["varlen_resume"] = bench_varlen(K, G)

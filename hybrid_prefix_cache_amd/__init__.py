@@ -36,8 +36,8 @@ EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset"
            "kda_prefill_workspace_bytes", "kda_prefill_chunked", "kda_decode_step",
            "kda_decode_verify",
            "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
-           "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8", "kda_profile_enable",
-           "kda_profile_read")
+           "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8",
+           "kda_conv_workspace_bytes", "kda_short_conv", "kda_profile_enable", "kda_profile_read")
 
 
 class KdaError(RuntimeError):
@@ -50,6 +50,12 @@ class kda_pool(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("page_bytes", ctypes.c_int64),
                 ("num_pages", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+class kda_conv_pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("page_bytes", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class kda_kernel_stat(ctypes.Structure):
@@ -82,6 +88,9 @@ _sig = {
     "kda_ckpt_int8_head_bytes": (ctypes.c_int64, [_i32, _i32]),
     "kda_checkpoint_write_int8": (ctypes.c_int, [_PP, _P, _PP, _P, _i32, _P]),
     "kda_checkpoint_restore_int8": (ctypes.c_int, [_PP, _P, _PP, _P, _i32, _P]),
+    "kda_conv_workspace_bytes": (_i64, [_i32, _i32]),
+    "kda_short_conv": (ctypes.c_int, [ctypes.POINTER(kda_conv_pool), _P, _P, _P, ctypes.c_int, _i32,
+                                      _P, _P, _P, _P, _P, _P, _P, _i32, _P, _sz, _P]),
     "kda_profile_enable": (ctypes.c_int, [_i32]),
     "kda_profile_read": (_i32, [ctypes.POINTER(kda_kernel_stat), _i32, _i32]),
 }
@@ -147,6 +156,12 @@ def make_pool(base, page_bytes: int, num_pages: int, num_heads: int, d_k: int, d
     device pointer)."""
     return kda_pool(_dptr(base), int(page_bytes), int(num_pages), int(num_heads), int(d_k),
                     int(d_k if d_v is None else d_v))
+
+
+def make_conv_pool(base, page_bytes: int, num_pages: int, channels: int, width: int, dtype: int):
+    """Conv-window pool descriptor over caller-owned device memory."""
+    return kda_conv_pool(_dptr(base), int(page_bytes), int(num_pages), int(channels), int(width),
+                         int(dtype))
 
 
 # ---------------------------------------------------------------------------
@@ -253,6 +268,35 @@ def kda_checkpoint_restore_int8(qpool, src_qckpt, pool, dst_active, *, stream=No
     s, d = _HostArr(src_qckpt, np.int32), _HostArr(dst_active, np.int32)
     _check(_lib.kda_checkpoint_restore_int8(ctypes.byref(qpool), s.ptr, ctypes.byref(pool), d.ptr,
                                             len(s.a), _stream(stream)))
+
+
+def kda_conv_workspace_bytes(num_seqs: int, num_ckpts: int) -> int:
+    return int(_lib.kda_conv_workspace_bytes(num_seqs, num_ckpts))
+
+
+def kda_short_conv(cpool, x, w, y, cu_seqlens, *, start_pos=None, state_in_page=None,
+                   state_out_page=None, ckpt_cu=None, ckpt_pos=None, ckpt_page=None,
+                   hash_block=HASH_BLOCK, workspace=None, workspace_bytes=None, out_dtype=None,
+                   stream=None):
+    """x, y: [T, C] device tensors (x in the pool's dtype); w: [C, W] fp32 device
+    tensor; host metadata as for kda_prefill_chunked.  The workspace is a device
+    uint8 tensor of at least kda_conv_workspace_bytes."""
+    cu = _HostArr(cu_seqlens, np.int64)
+    ns = len(cu.a) - 1
+    sp = _HostArr(start_pos, np.int64)
+    si = _HostArr(state_in_page, np.int32)
+    so = _HostArr(state_out_page, np.int32)
+    ccu = _HostArr(ckpt_cu, np.int32)
+    cpos = _HostArr(ckpt_pos, np.int64)
+    cpg = _HostArr(ckpt_page, np.int32)
+    outd = _dtype_code(y) if out_dtype is None else out_dtype
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else (
+            workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0)
+    st = _lib.kda_short_conv(ctypes.byref(cpool), _dptr(x), _dptr(w), _dptr(y), outd, ns, cu.ptr,
+                             sp.ptr, si.ptr, so.ptr, ccu.ptr, cpos.ptr, cpg.ptr, hash_block,
+                             _dptr(workspace), workspace_bytes, _stream(stream))
+    _check(st)
 
 
 def kda_profile_enable(on: bool = True):

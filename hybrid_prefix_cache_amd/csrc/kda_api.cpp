@@ -437,6 +437,143 @@ kda_status kda_checkpoint_restore(const kda_pool* pool, const int32_t* src_ckpt,
   return copy_pages("kda_checkpoint_restore", pool, src_ckpt, dst_active, n, stream);
 }
 
+// ---- short causal convolution --------------------------------------------------
+
+int64_t kda_conv_workspace_bytes(int32_t num_seqs, int32_t num_ckpts) {
+  if (num_seqs < 0 || num_ckpts < 0) return -1;
+  return meta_layout(num_seqs, num_ckpts).inter_off;
+}
+
+static kda_status check_conv_pool(const kda_conv_pool* p) {
+  if (!p) return fail(KDA_ERR_NULL, "kda_short_conv: conv pool descriptor is NULL");
+  if (!p->base) return fail(KDA_ERR_POOL, "kda_short_conv: conv pool base is NULL");
+  if (!aligned(p->base, 256)) return fail(KDA_ERR_POOL, "kda_short_conv: conv pool base must be 256-byte aligned");
+  if (p->num_pages < 1) return fail(KDA_ERR_POOL, "kda_short_conv: conv pool needs num_pages >= 1");
+  if (p->width < 2 || p->width > 4) return fail(KDA_ERR_SHAPE, "kda_short_conv: width %d not in {2, 3, 4}", p->width);
+  if (!valid_dtype(p->dtype)) return fail(KDA_ERR_DTYPE, "kda_short_conv: unknown dtype code %d", p->dtype);
+  const int vec = p->dtype == KDA_BF16 ? 8 : 4;
+  if (p->channels < vec || p->channels % vec != 0 || p->channels > (1 << 24))
+    return fail(KDA_ERR_SHAPE, "kda_short_conv: channels %d must be a positive multiple of %d", p->channels, vec);
+  const int64_t need = (int64_t)(p->width - 1) * p->channels * (p->dtype == KDA_BF16 ? 2 : 4);
+  if (p->page_bytes < need || p->page_bytes % 256 != 0)
+    return fail(KDA_ERR_POOL, "kda_short_conv: page_bytes %lld must be a multiple of 256 and >= %lld",
+                (long long)p->page_bytes, (long long)need);
+  return KDA_OK;
+}
+
+kda_status kda_short_conv(const kda_conv_pool* cpool, const void* x, const float* w, void* y,
+                          kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
+                          const int64_t* start_pos, const int32_t* state_in_page,
+                          const int32_t* state_out_page, const int32_t* ckpt_cu,
+                          const int64_t* ckpt_pos, const int32_t* ckpt_page, int32_t hash_block,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "kda_short_conv";
+  kda_status s = check_conv_pool(cpool);
+  if (s != KDA_OK) return s;
+  if (!valid_dtype(out_dtype)) return fail(KDA_ERR_DTYPE, "%s: unknown out dtype %d", what, (int)out_dtype);
+  if (hash_block <= 0 || hash_block % 64 != 0)
+    return fail(KDA_ERR_SHAPE, "%s: hash_block must be a positive multiple of 64 (got %d)", what, hash_block);
+  if (num_seqs < 0) return fail(KDA_ERR_SEQ, "%s: num_seqs < 0", what);
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens) return fail(KDA_ERR_NULL, "%s: cu_seqlens is NULL", what);
+  if (cu_seqlens[0] != 0) return fail(KDA_ERR_SEQ, "%s: cu_seqlens[0] must be 0", what);
+  const int32_t P = cpool->num_pages;
+  int64_t total_chunks = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t len = cu_seqlens[i + 1] - cu_seqlens[i];
+    if (len < 0) return fail(KDA_ERR_SEQ, "%s: cu_seqlens decreases at %d", what, i);
+    if (len > (int64_t)1 << 30) return fail(KDA_ERR_SEQ, "%s: sequence %d longer than 2^30", what, i);
+    const int64_t sp = start_pos ? start_pos[i] : 0;
+    if (sp < 0) return fail(KDA_ERR_SEQ, "%s: start_pos[%d] < 0", what, i);
+    const int32_t po = state_out_page ? state_out_page[i] : -1;
+    total_chunks += len > 0 ? (len + 63) / 64 : (po >= 0 ? 1 : 0);
+  }
+  if (total_chunks > (int64_t)1 << 28) return fail(KDA_ERR_SEQ, "%s: too many tokens", what);
+  const int64_t total_tokens = cu_seqlens[num_seqs];
+  if (total_tokens > 0 && (!x || !y)) return fail(KDA_ERR_NULL, "%s: x and y must be non-NULL", what);
+  if (!w) return fail(KDA_ERR_NULL, "%s: weights are NULL", what);
+  for (const void* p : {x, static_cast<const void*>(y), static_cast<const void*>(w)})
+    if (p && !aligned(p, 16)) return fail(KDA_ERR_SHAPE, "%s: x, y, w must be 16-byte aligned", what);
+  if (x && x == y) return fail(KDA_ERR_SHAPE, "%s: y may not alias x", what);
+  const int32_t num_ckpts = ckpt_cu ? ckpt_cu[num_seqs] : 0;
+  if (ckpt_cu) {
+    if (ckpt_cu[0] != 0) return fail(KDA_ERR_CKPT_RANGE, "%s: ckpt_cu[0] must be 0", what);
+    if (num_ckpts > 0 && (!ckpt_pos || !ckpt_page)) return fail(KDA_ERR_NULL, "%s: ckpt_pos / ckpt_page are NULL", what);
+  }
+  std::unordered_set<int32_t> reads, writes;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t pi = state_in_page ? state_in_page[i] : -1;
+    const int32_t po = state_out_page ? state_out_page[i] : -1;
+    if (pi < -1 || pi >= P) return fail(KDA_ERR_PAGE_RANGE, "%s: state_in_page[%d] = %d", what, i, pi);
+    if (po < -1 || po >= P) return fail(KDA_ERR_PAGE_RANGE, "%s: state_out_page[%d] = %d", what, i, po);
+    if (pi >= 0) reads.insert(pi);
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t po = state_out_page ? state_out_page[i] : -1;
+    if (po >= 0) {
+      if (reads.count(po)) return fail(KDA_ERR_PAGE_ALIAS, "%s: output page %d is also an input page", what, po);
+      if (!writes.insert(po).second) return fail(KDA_ERR_PAGE_ALIAS, "%s: page %d written twice", what, po);
+    }
+    if (!ckpt_cu) continue;
+    if (ckpt_cu[i + 1] < ckpt_cu[i]) return fail(KDA_ERR_CKPT_RANGE, "%s: ckpt_cu decreases at %d", what, i);
+    const int64_t st = start_pos ? start_pos[i] : 0;
+    const int64_t len = cu_seqlens[i + 1] - cu_seqlens[i];
+    for (int32_t m = ckpt_cu[i]; m < ckpt_cu[i + 1]; ++m) {
+      const int64_t pos = ckpt_pos[m];
+      if (pos % hash_block != 0)
+        return fail(KDA_ERR_CKPT_ALIGN, "%s: checkpoint %d at %lld is not a multiple of %d", what, m,
+                    (long long)pos, hash_block);
+      if (pos <= st || pos > st + len || (m > ckpt_cu[i] && pos <= ckpt_pos[m - 1]))
+        return fail(KDA_ERR_CKPT_RANGE, "%s: checkpoint %d at %lld outside (%lld, %lld] or unordered", what,
+                    m, (long long)pos, (long long)st, (long long)(st + len));
+      const int32_t pg = ckpt_page[m];
+      if (pg < 0 || pg >= P) return fail(KDA_ERR_PAGE_RANGE, "%s: ckpt_page[%d] = %d", what, m, pg);
+      if (reads.count(pg)) return fail(KDA_ERR_PAGE_ALIAS, "%s: checkpoint page %d is also an input page", what, pg);
+      if (!writes.insert(pg).second) return fail(KDA_ERR_PAGE_ALIAS, "%s: page %d written twice", what, pg);
+    }
+  }
+  const MetaLayout ml = meta_layout(num_seqs, num_ckpts);
+  if (!workspace) return fail(KDA_ERR_WORKSPACE, "%s: workspace is NULL", what);
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", what);
+  if ((int64_t)workspace_bytes < ml.inter_off)
+    return fail(KDA_ERR_WORKSPACE, "%s: workspace too small: %zu < %lld bytes", what, workspace_bytes,
+                (long long)ml.inter_off);
+  if (total_chunks == 0) return ok();
+
+  std::vector<uint8_t> blob((size_t)ml.inter_off, 0);
+  SeqEntry* seqs = reinterpret_cast<SeqEntry*>(blob.data() + ml.seq_off);
+  int32_t cb = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    SeqEntry& e = seqs[i];
+    e.row_begin = cu_seqlens[i];
+    e.start_pos = start_pos ? start_pos[i] : 0;
+    e.len = (int32_t)(cu_seqlens[i + 1] - cu_seqlens[i]);
+    e.chunk_begin = cb;
+    e.state_in = state_in_page ? state_in_page[i] : -1;
+    e.state_out = state_out_page ? state_out_page[i] : -1;
+    cb += e.len > 0 ? (e.len + 63) / 64 : (e.state_out >= 0 ? 1 : 0);
+    e.ckpt_begin = ckpt_cu ? ckpt_cu[i] : 0;
+    e.ckpt_end = ckpt_cu ? ckpt_cu[i + 1] : 0;
+  }
+  CkptEntry* ck = reinterpret_cast<CkptEntry*>(blob.data() + ml.ckpt_off);
+  for (int32_t m = 0; m < num_ckpts; ++m) {
+    ck[m].pos = ckpt_pos[m];
+    ck[m].page = ckpt_page[m];
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  s = ship_metadata(ws, blob, st);
+  if (s != KDA_OK) return s;
+  ConvArgs a{x, w, y, reinterpret_cast<const SeqEntry*>(ws + ml.seq_off),
+             reinterpret_cast<const CkptEntry*>(ws + ml.ckpt_off), static_cast<uint8_t*>(cpool->base),
+             cpool->page_bytes, num_seqs, cpool->channels, cpool->width, cpool->dtype == KDA_BF16,
+             out_dtype == KDA_BF16, hash_block};
+  Launch L("kda_short_conv", st);
+  hipError_t e = launch_conv(a, (int32_t)total_chunks, st);
+  if (e != hipSuccess) return hip_fail(e, "conv launch");
+  return ok();
+}
+
 // ---- int8 compressed checkpoints ----------------------------------------------
 
 int64_t kda_ckpt_int8_head_bytes(int32_t d_k, int32_t d_v) {

@@ -92,7 +92,37 @@ hipError_t launch_meta_fill(const MetaFillArgs& a, hipStream_t st);
 hipError_t launch_prep(int D, bool bf16, const PrepArgs& a, int total_chunks, hipStream_t st);
 hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st);
 hipError_t launch_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t st);
+// Sequence owning a global chunk index: the largest s with
+// seqs[s].chunk_begin <= chunk (chunk tables are increasing).
+__device__ __forceinline__ int find_seq(const SeqEntry* seqs, int n, int chunk) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (seqs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One kda_short_conv call: 16-token blocks of the 64-token chunks of the
+// sequence table, by channel groups.
+struct ConvArgs {
+  const void* x;
+  const float* w;
+  void* y;
+  const SeqEntry* seqs;
+  const CkptEntry* ckpts;
+  uint8_t* cpool;
+  int64_t cpage_bytes;
+  int32_t num_seqs;
+  int32_t C;
+  int32_t W;
+  int32_t in_bf16;
+  int32_t out_bf16;
+  int32_t hash_block;
+};
+
 hipError_t launch_copy(const CopyArgs& a, hipStream_t st);
+hipError_t launch_conv(const ConvArgs& a, int32_t total_chunks, hipStream_t st);
 hipError_t launch_quant(int D, const QuantArgs& a, hipStream_t st);
 hipError_t launch_dequant(int D, const QuantArgs& a, hipStream_t st);
 

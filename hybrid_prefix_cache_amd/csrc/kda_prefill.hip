@@ -74,15 +74,6 @@ __device__ __forceinline__ void store8(float* p, const float* x) {
 
 // Largest s with seqs[s].chunk_begin <= chunk: the sequence owning `chunk`
 // (zero-length sequences share their successor's chunk_begin).
-__device__ __forceinline__ int find_seq(const SeqEntry* seqs, int n, int chunk) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (seqs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // Offsets (in Op elements) of the pieces of one (chunk, head) block.  Every
 // piece is stored fragment-major (see frag_off) as the scan's MFMA operand:
 // Keff, Qeff, T, P by token rows, KendT by channel rows.

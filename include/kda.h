@@ -263,6 +263,56 @@ kda_status kda_checkpoint_restore_int8(const kda_pool* qpool, const int32_t* src
                                        void* stream);
 
 /*
+ * Short causal convolution with a checkpointed window state [CONV]: page
+ * "KIMI K3 경량 복제에서 본 KDA의 AI 인프라 과제" (acpost.vercel.app), sections
+ * 6.5 and 8.2.3/8.2.4: before the recurrence, q, k and v each pass through a
+ * short causal convolution whose state is the window of the most recent inputs;
+ * that window is checkpointed with the recurrent state at the same boundary,
+ * kept at full precision, and a restore must bring it back too.  The pages fix
+ * neither the width nor an activation; this build takes a width W in {2, 3, 4}
+ * and no activation:
+ *     y[t][c] = sum_{j < W} w[c][j] * x[t - (W-1) + j][c]
+ * with x at positions before a sequence's start taken from its state page
+ * (zeros when there is none).  Call it once per tensor (q, k, v).
+ *
+ * Conv-state pool: page p holds the W-1 most recent inputs, token-major
+ * ([W-1][channels], row i = the input at position P-(W-1)+i), in `dtype` (the
+ * input dtype).  page_bytes >= (W-1) * channels * elem, multiple of 256.
+ */
+typedef struct {
+  void* base;          /* device memory, 256-byte aligned */
+  int64_t page_bytes;
+  int32_t num_pages;
+  int32_t channels;    /* C: channels per token, e.g. H * d for one of q, k, v */
+  int32_t width;       /* W in {2, 3, 4} */
+  int32_t dtype;       /* kda_dtype of x and of the stored window */
+} kda_conv_pool;
+
+/* Workspace bytes (per-call metadata tables) of kda_short_conv. */
+int64_t kda_conv_workspace_bytes(int32_t num_seqs, int32_t num_ckpts);
+
+/*
+ * x : [T, C] (cpool->dtype, device), w : [C][W] fp32 (device), y : [T, C]
+ * (out_dtype, device; may not alias x).  Sequences as in kda_prefill_chunked:
+ * cu_seqlens [num_seqs+1] int64 host; start_pos [num_seqs] host or NULL (any
+ * non-negative value); state_in_page / state_out_page [num_seqs] int32 host or
+ * NULL (-1 = zero window / not written); checkpoints (ckpt_cu, ckpt_pos,
+ * ckpt_page, host) at multiples of hash_block inside (start, start+len] receive
+ * the window of the hash_block-aligned position, written in the same pass.  An
+ * empty sequence with an output page copies its input window.  Output pages
+ * and checkpoint pages are distinct and are never input pages of the call.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_POOL, KDA_ERR_SEQ,
+ * KDA_ERR_PAGE_RANGE, KDA_ERR_PAGE_ALIAS, KDA_ERR_CKPT_ALIGN, KDA_ERR_CKPT_RANGE,
+ * KDA_ERR_WORKSPACE, KDA_ERR_HIP.
+ */
+kda_status kda_short_conv(const kda_conv_pool* cpool, const void* x, const float* w, void* y,
+                          kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
+                          const int64_t* start_pos, const int32_t* state_in_page,
+                          const int32_t* state_out_page, const int32_t* ckpt_cu,
+                          const int64_t* ckpt_pos, const int32_t* ckpt_page, int32_t hash_block,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-kernel timing (tracing aid).  When enabled, every kernel the
  * library launches is bracketed by a pair of HIP events on its own stream;
  * kda_profile_read synchronises those events and returns, per kernel name, the

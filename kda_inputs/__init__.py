@@ -35,6 +35,7 @@ DTYPES = {"f32": (F32, np.float32), "bf16": (BF16, np.uint16), "f64": (F64, np.f
 
 # stream ids (low 8 bits) per tensor; bits 8.. carry the sequence / request id
 TID_Q, TID_K, TID_V, TID_G, TID_BETA, TID_STATE, TID_PLAN = 1, 2, 3, 4, 5, 6, 7
+TID_CONV_X, TID_CONV_W = 8, 9
 
 
 def build() -> str:
@@ -133,6 +134,20 @@ def random_states(seed, n, H, D, seq_id=0, threads=0):
     st = fill(seed, stream_id(TID_STATE, seq_id), NORMAL, 0, n * H, D, D, "f32",
               scale=1.0 / np.sqrt(D), threads=threads)
     return st.reshape(n, H, D, D)
+
+
+def conv_inputs(seed, T, C, dtype="bf16", threads=0):
+    """Pre-convolution activations (one of the q, k, v projections): N(0, 1),
+    [T, C] in the stored dtype."""
+    H = next(h for h in range(1, C + 1) if C % h == 0 and C // h <= 1024)  # rows of <= 1024
+    return fill(seed, stream_id(TID_CONV_X), NORMAL, 0, T, H, C // H, dtype,
+                threads=threads).reshape(T, C)
+
+
+def conv_weights(seed, C, W):
+    """Short-convolution taps, N(0, 1/W) fp32 -> float32 [C, W]."""
+    return fill(seed, stream_id(TID_CONV_W), NORMAL, 0, C, 1, W, "f32",
+                scale=1.0 / np.sqrt(W)).reshape(C, W)
 
 
 from .workloads import *  # noqa: E402,F401,F403

@@ -261,3 +261,87 @@ def test_verify_validation():
     assert call(-1, 2) == K.KDA_ERR_SHAPE
     assert call(4, 2, pout=None) == K.KDA_ERR_NULL
     assert call(0, 2, None, None) == K.KDA_OK  # no requests: nothing to do
+
+
+def cpool(**kw):
+    d = dict(base=FAKE, page_bytes=4096, num_pages=16, channels=512, width=4, dtype=K.KDA_BF16)
+    d.update(kw)
+    return K.make_conv_pool(d["base"], d["page_bytes"], d["num_pages"], d["channels"], d["width"],
+                            d["dtype"])
+
+
+def _conv_status(cp=None, T=1024, **kw):
+    cp = cp or cpool()
+    args = dict(x=FAKE, w=FAKE, y=FAKE + MiB2, cu_seqlens=[0, T], out_dtype=K.KDA_BF16,
+                workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+    args.update(kw)
+    x, w, y = args.pop("x"), args.pop("w"), args.pop("y")
+    try:
+        K.kda_short_conv(cp, x, w, y, **args)
+    except K.KdaError as e:
+        assert K.kda_last_error() != ""
+        return e.status
+    return K.KDA_OK
+
+
+def test_conv_workspace_bytes():
+    assert K.kda_conv_workspace_bytes(-1, 0) == -1
+    a, b = K.kda_conv_workspace_bytes(4, 0), K.kda_conv_workspace_bytes(4, 100)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+
+
+@pytest.mark.parametrize("pkw,status", [
+    (dict(width=1), K.KDA_ERR_SHAPE),
+    (dict(width=5), K.KDA_ERR_SHAPE),
+    (dict(channels=0), K.KDA_ERR_SHAPE),
+    (dict(channels=12), K.KDA_ERR_SHAPE),                     # bf16 needs a multiple of 8
+    (dict(channels=6, dtype=K.KDA_F32), K.KDA_ERR_SHAPE),     # fp32 needs a multiple of 4
+    (dict(dtype=3), K.KDA_ERR_DTYPE),
+    (dict(base=0), K.KDA_ERR_POOL),
+    (dict(base=FAKE + 16), K.KDA_ERR_POOL),
+    (dict(num_pages=0), K.KDA_ERR_POOL),
+    (dict(page_bytes=2816), K.KDA_ERR_POOL),                  # 3 * 512 * 2 = 3072 needed
+    (dict(page_bytes=3100), K.KDA_ERR_POOL),                  # not a multiple of 256
+])
+def test_conv_pool_validation(pkw, status):
+    assert _conv_status(cp=cpool(**pkw)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out_dtype=9), K.KDA_ERR_DTYPE),
+    (dict(hash_block=100), K.KDA_ERR_SHAPE),
+    (dict(x=0), K.KDA_ERR_NULL),
+    (dict(w=0), K.KDA_ERR_NULL),
+    (dict(y=FAKE + 8), K.KDA_ERR_SHAPE),
+    (dict(y=FAKE), K.KDA_ERR_SHAPE),                          # y aliases x
+    (dict(cu_seqlens=[2, 10]), K.KDA_ERR_SEQ),
+    (dict(cu_seqlens=[0, 10, 5]), K.KDA_ERR_SEQ),
+    (dict(start_pos=[-1]), K.KDA_ERR_SEQ),
+    (dict(state_in_page=[16]), K.KDA_ERR_PAGE_RANGE),
+    (dict(state_out_page=[-3]), K.KDA_ERR_PAGE_RANGE),
+    (dict(state_in_page=[2], state_out_page=[2]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(cu_seqlens=[0, 5, 9], state_out_page=[4, 4]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[500], ckpt_page=[3]), K.KDA_ERR_CKPT_ALIGN),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[1536], ckpt_page=[3]), K.KDA_ERR_CKPT_RANGE),
+    (dict(start_pos=[512], ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[3]), K.KDA_ERR_CKPT_RANGE),
+    (dict(ckpt_cu=[0, 2], ckpt_pos=[1024, 512], ckpt_page=[3, 4]), K.KDA_ERR_CKPT_RANGE),
+    (dict(ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[99]), K.KDA_ERR_PAGE_RANGE),
+    (dict(state_in_page=[3], ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[3]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(state_out_page=[3], ckpt_cu=[0, 1], ckpt_pos=[512], ckpt_page=[3]), K.KDA_ERR_PAGE_ALIAS),
+    (dict(workspace=0), K.KDA_ERR_WORKSPACE),
+    (dict(workspace=FAKE + 32), K.KDA_ERR_WORKSPACE),
+    (dict(workspace_bytes=16), K.KDA_ERR_WORKSPACE),
+])
+def test_conv_validation(kw, status):
+    assert _conv_status(**kw) == status
+
+
+def test_conv_accepts_checkpoints_past_start_and_empty_batch():
+    # a start inside a block: the checkpoint at the next boundary is in range
+    assert _conv_status(start_pos=[700], ckpt_cu=[0, 1], ckpt_pos=[1024], ckpt_page=[3],
+                        workspace=0) == K.KDA_ERR_WORKSPACE  # everything before the workspace passed
+    st = K.raw_call("kda_short_conv", ctypes.byref(cpool()), None, ctypes.c_void_p(FAKE), None,
+                    K.KDA_BF16, 0, None, None, None, None, None, None, None, 512, None, 0, None)
+    assert st == K.KDA_OK
+    # empty sequences without output pages enqueue nothing
+    assert _conv_status(T=0, x=0, y=0) == K.KDA_OK

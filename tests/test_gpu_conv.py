@@ -1,0 +1,206 @@
+"""GPU parity of kda_short_conv against oracle/conv.py: outputs within the fp32
+rounding bound of the fp64 oracle (plus one bf16 rounding for bf16 outputs),
+element by element; final and checkpoint windows bit-exact; pages outside the
+call untouched; a split call and a resume from a checkpoint window reproduce
+the single call bit for bit; the 8192 x 4096 workload the bench times at full
+size."""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_prefix_cache_amd as K
+import kda_inputs as G
+from kda_gpu_util import POISON_WORD, rel_fro
+from oracle import conv
+
+pytestmark = pytest.mark.gpu
+POISON = np.int32(np.uint32(POISON_WORD).view(np.int32))
+U32 = 2.0 ** -24   # fp32 unit roundoff
+UBF = 2.0 ** -8    # bf16 unit roundoff (8 significant bits)
+
+
+def to64(x, dtype):
+    """Generator output (bf16 bits or fp32) -> float64 values."""
+    if dtype == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def to_bits(v, dtype):
+    """Exactly representable float64 values -> stored words (uint16 bf16 bits / fp32)."""
+    if dtype == "bf16":
+        f = v.astype(np.float32)
+        assert np.array_equal(f.astype(np.float64), v)
+        bits = f.view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0), "not a bf16 value"
+        return (bits >> 16).astype(np.uint16)
+    return v.astype(np.float32)
+
+
+def dev(x, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+class ConvPool:
+    """A poisoned device region of conv-window pages."""
+
+    def __init__(self, num_pages, C, W, dtype, extra=256):
+        self.C, self.W, self.dtype = C, W, dtype
+        self.elem = 2 if dtype == "bf16" else 4
+        self.win_bytes = (W - 1) * C * self.elem
+        self.page_bytes = (self.win_bytes + extra + 255) // 256 * 256
+        self.buf = torch.full((num_pages * self.page_bytes // 4,), int(POISON), dtype=torch.int32,
+                              device="cuda")
+        code = K.KDA_BF16 if dtype == "bf16" else K.KDA_F32
+        self.pool = K.make_conv_pool(self.buf, self.page_bytes, num_pages, C, W, code)
+
+    def _bytes(self, p):
+        return self.buf.view(torch.uint8)[p * self.page_bytes:(p + 1) * self.page_bytes]
+
+    def set_window(self, p, v64):
+        raw = np.ascontiguousarray(to_bits(v64, self.dtype)).view(np.uint8).reshape(-1)
+        self._bytes(p)[:self.win_bytes].copy_(torch.from_numpy(raw))
+
+    def window_bits(self, p):
+        raw = self._bytes(p).cpu().numpy()
+        w = raw[:self.win_bytes].view(np.uint16 if self.dtype == "bf16" else np.float32)
+        return w.reshape(self.W - 1, self.C), raw[self.win_bytes:]
+
+
+def run_conv(cp, x_dev, w_dev, cu, out_dtype, **kw):
+    T = int(cu[-1])
+    y = torch.full((T, cp.C), float("nan"), device="cuda",
+                   dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    nck = 0 if kw.get("ckpt_cu") is None else int(kw["ckpt_cu"][-1])
+    ws = torch.empty(max(256, K.kda_conv_workspace_bytes(len(cu) - 1, nck)), dtype=torch.uint8,
+                     device="cuda")
+    K.kda_short_conv(cp.pool, x_dev, w_dev, y, cu, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def err_bound(x64, w64, cu, windows_in, out_dtype, ref):
+    """Per-element bound: W fused multiply-adds in fp32 against the fp64 sum,
+    plus one bf16 rounding of the fp32 result for bf16 outputs."""
+    W = w64.shape[1]
+    mag = np.zeros_like(ref)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        m, _ = conv.conv_segment(np.abs(x64[a:b]), np.abs(w64),
+                                 None if windows_in[s] is None else np.abs(windows_in[s]))
+        mag[a:b] = m
+    fp32 = (W + 1) * U32 * mag + 1e-30
+    return fp32 + (UBF * (np.abs(ref) + fp32) if out_dtype == "bf16" else 0.0)
+
+
+def check_windows(cp, page, expect64, tag):
+    got, tail = cp.window_bits(page)
+    assert np.array_equal(got.view(np.uint8), to_bits(expect64, cp.dtype).view(np.uint8)), tag
+    assert np.all(tail.view(np.int32) == POISON), f"{tag}: page tail overwritten"
+
+
+# lens / starts: single token, ragged chunks, exactly one chunk, a boundary one
+# token in, 512 crossed mid-block, two boundaries, empty sequences with and
+# without an entering window.
+LENS = [1, 63, 64, 65, 700, 1030, 0, 17, 0]
+STARTS = [0, 5, 512, 448, 100, 1000, 30, 3, 0]
+STATE_IN = [-1, 0, -1, 1, -1, 2, 3, -1, -1]
+
+
+@pytest.mark.parametrize("dtype,out_dtype,W", [
+    ("bf16", "bf16", 2), ("bf16", "bf16", 3), ("bf16", "bf16", 4),
+    ("f32", "f32", 2), ("f32", "f32", 3), ("f32", "f32", 4), ("bf16", "f32", 3)])
+def test_conv_parity_varlen(dtype, out_dtype, W):
+    C = 2400 if dtype == "bf16" else 1200   # 300 channel groups: one full and one partial column
+    cu = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int64)
+    T = int(cu[-1])
+    seed = 40 + W
+    x = G.conv_inputs(seed, T, C, dtype)
+    w = G.conv_weights(seed, C, W)
+    x64, w64 = to64(x, dtype), w.astype(np.float64)
+    wins = G.conv_inputs(seed + 1000, 4 * (W - 1), C, dtype)
+    cp = ConvPool(40, C, W, dtype)
+    windows_in = []
+    for s, p in enumerate(STATE_IN):
+        if p >= 0:
+            v = to64(wins[p * (W - 1):(p + 1) * (W - 1)], dtype)
+            cp.set_window(p, v)
+            windows_in.append(v)
+        else:
+            windows_in.append(None)
+    state_out = [-1] + [10 + s for s in range(1, len(LENS))]
+    ckpts, ckpt_pages = [], []
+    nxt = 25
+    for s in range(len(LENS)):
+        ps = [P for P in range(512, STARTS[s] + LENS[s] + 1, 512) if P > STARTS[s]]
+        ckpts.append(ps)
+        ckpt_pages.append(list(range(nxt, nxt + len(ps))))
+        nxt += len(ps)
+    assert sum(map(len, ckpts)) == 4
+    ckpt_cu = np.concatenate([[0], np.cumsum([len(c) for c in ckpts])]).astype(np.int32)
+    y = run_conv(cp, dev(x, dtype), torch.from_numpy(w).cuda(), cu, out_dtype,
+                 start_pos=STARTS, state_in_page=STATE_IN, state_out_page=state_out,
+                 ckpt_cu=ckpt_cu, ckpt_pos=[P for c in ckpts for P in c],
+                 ckpt_page=[p for c in ckpt_pages for p in c])
+    ref, finals, ck = conv.short_conv_varlen(x64, w64, cu, STARTS, windows_in, ckpts)
+    bound = err_bound(x64, w64, cu, windows_in, out_dtype, ref)
+    bad = np.abs(y - ref) > bound
+    assert not bad.any(), f"{bad.sum()} elements outside the rounding bound, first at {np.argwhere(bad)[0]}"
+    assert rel_fro(y, ref) <= (1e-5 if out_dtype == "f32" else 4e-3)
+    for s in range(len(LENS)):
+        if state_out[s] >= 0:
+            check_windows(cp, state_out[s], finals[s], f"final window of sequence {s}")
+        for P, pg, v in zip(ckpts[s], ckpt_pages[s], ck[s]):
+            check_windows(cp, pg, v, f"checkpoint {P} of sequence {s}")
+    # the empty sequence without an entering window leaves a zero window
+    assert np.all(finals[8] == 0)
+    # pages the call neither read nor wrote keep their poison
+    written = {p for p in state_out if p >= 0} | {p for c in ckpt_pages for p in c}
+    words = cp.buf.cpu().numpy().reshape(40, -1)
+    for p in range(40):
+        if p not in written and p not in STATE_IN:
+            assert np.all(words[p] == POISON), f"page {p} touched"
+
+
+def test_conv_split_and_resume_bitwise():
+    """A sequence run in one call, in two calls joined by the window page, and
+    resumed from its checkpoint window at 1024 gives identical bits."""
+    dtype, W, C, T = "bf16", 4, 1024, 1500
+    x = G.conv_inputs(7, T, C, dtype)
+    w = torch.from_numpy(G.conv_weights(7, C, W)).cuda()
+    xd = dev(x, dtype)
+    cp = ConvPool(8, C, W, dtype)
+    whole = run_conv(cp, xd, w, [0, T], "bf16", state_out_page=[0], ckpt_cu=[0, 2],
+                     ckpt_pos=[512, 1024], ckpt_page=[1, 2])
+    a = run_conv(cp, xd[:700], w, [0, 700], "bf16", state_out_page=[3])
+    b = run_conv(cp, xd[700:], w, [0, T - 700], "bf16", start_pos=[700], state_in_page=[3],
+                 state_out_page=[4])
+    assert np.array_equal(np.concatenate([a, b]), whole)
+    r = run_conv(cp, xd[1024:], w, [0, T - 1024], "bf16", start_pos=[1024], state_in_page=[2],
+                 state_out_page=[5])
+    assert np.array_equal(r, whole[1024:])
+    for p in (4, 5):
+        assert np.array_equal(cp.window_bits(p)[0], cp.window_bits(0)[0])
+
+
+def test_conv_full_size_8k():
+    """The bench workload: one of q, k, v for 8192 tokens x 32 heads x 128
+    channels, width 4, a checkpoint at every 512-token boundary."""
+    dtype, W, C, T = "bf16", 4, 32 * 128, 8192
+    x = G.conv_inputs(3, T, C, dtype)
+    w = G.conv_weights(3, C, W)
+    cp = ConvPool(20, C, W, dtype, extra=0)
+    P = list(range(512, T + 1, 512))
+    y = run_conv(cp, dev(x, dtype), torch.from_numpy(w).cuda(), [0, T], "bf16",
+                 state_out_page=[0], ckpt_cu=[0, len(P)], ckpt_pos=P,
+                 ckpt_page=list(range(1, 1 + len(P))))
+    x64, w64 = to64(x, dtype), w.astype(np.float64)
+    ref, finals, ck = conv.short_conv_varlen(x64, w64, [0, T], None, None, [P])
+    bound = err_bound(x64, w64, [0, T], [None], "bf16", ref)
+    assert not (np.abs(y - ref) > bound).any()
+    got, _ = cp.window_bits(0)
+    assert np.array_equal(got, to_bits(finals[0], dtype))
+    for i, v in enumerate(ck[0]):
+        assert np.array_equal(cp.window_bits(1 + i)[0], to_bits(v, dtype)), f"checkpoint {P[i]}"
