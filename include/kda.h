@@ -265,7 +265,7 @@ kda_status kda_checkpoint_restore_int8(const kda_pool* qpool, const int32_t* src
 /*
  * Short causal convolution with a checkpointed window state [CONV]: page
  * "KIMI K3 경량 복제에서 본 KDA의 AI 인프라 과제" (acpost.vercel.app), sections
- * 6.5 and 8.2.3/8.2.4: before the recurrence, q, k and v each pass through a
+ * 1.1, 6.5, 6.6.3 and 8.2.3/8.2.4: before the recurrence, q, k and v each pass through a
  * short causal convolution whose state is the window of the most recent inputs;
  * that window is checkpointed with the recurrent state at the same boundary,
  * kept at full precision, and a restore must bring it back too.  The pages fix

@@ -2,8 +2,8 @@
 rounding bound of the fp64 oracle (plus one bf16 rounding for bf16 outputs),
 element by element; final and checkpoint windows bit-exact; pages outside the
 call untouched; a split call and a resume from a checkpoint window reproduce
-the single call bit for bit; the 8192 x 4096 workload the bench times at full
-size."""
+the single call bit for bit; the fused q|k|v workload the bench times
+(8192 tokens x 12288 channels) at full size."""
 import numpy as np
 import pytest
 import torch
@@ -186,9 +186,10 @@ def test_conv_split_and_resume_bitwise():
 
 
 def test_conv_full_size_8k():
-    """The bench workload: one of q, k, v for 8192 tokens x 32 heads x 128
-    channels, width 4, a checkpoint at every 512-token boundary."""
-    dtype, W, C, T = "bf16", 4, 32 * 128, 8192
+    """The bench workload: the fused q|k|v projection of 8192 tokens
+    (3 x 32 heads x 128 channels), width 4, a checkpoint at every 512-token
+    boundary."""
+    dtype, W, C, T = "bf16", 4, 3 * 32 * 128, 8192
     x = G.conv_inputs(3, T, C, dtype)
     w = G.conv_weights(3, C, W)
     cp = ConvPool(20, C, W, dtype, extra=0)
