@@ -433,6 +433,78 @@ def bench_conv(K, G, steps=20, warmup=5, T=8192, C=3 * 32 * 128, W=4):
             "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_index(K, G, reps=100):
+    """Host prefix index (no GPU): a 2^20-token session in 6144-token pages with
+    a checkpoint every 6144 tokens in 2 KDA groups, plus 64 agentic sessions of
+    32,768 tokens sharing a 4096-token system prompt (a checkpoint every 4096
+    tokens).  Timed: lookup + pin + release of the long session diverging at
+    900,000 tokens, and of each short session diverging at a random point; the
+    oracle (token-prefix comparison, no hashing) on a sample of the short ones."""
+    from oracle.prefix_index import PrefixIndexModel
+    hb, pb, groups = 512, 6144, 2
+    idx = K.kda_index_create(hb, pb, groups, namespace_seed=1)
+    model = PrefixIndexModel(hb, pb, groups)
+    ck = [1_000_000]
+
+    def add(t, every, page0, to_model):
+        npg = -(-len(t) // pb)
+        K.kda_index_register_pages(idx, t, list(range(page0, page0 + npg)))
+        if to_model:
+            model.register_pages(t, list(range(page0, page0 + npg)), 0)
+        for b in range(every, len(t) + 1, every):
+            for g in range(groups):
+                ck[0] += 1
+                K.kda_index_register_ckpt(idx, t, b, g, ck[0], durable=True)
+                if to_model:
+                    model.register_ckpt(t, b, g, ck[0], True, 0)
+        return page0 + npg
+
+    long_t = G.token_ids(21, 1 << 20)
+    page = add(long_t, pb, 0, False)
+    system = G.token_ids(22, 4096)
+    sessions = []
+    for s in range(64):
+        t = np.concatenate([system, G.token_ids(23, 32768 - 4096, seq_id=s)])
+        page = add(t, 4096, page, s < 8)
+        sessions.append(t)
+    K.kda_index_mark_ready(idx, 0)
+    model.mark_ready(0)
+    rng = np.random.default_rng(5)
+    req_long = np.concatenate([long_t[:900_000], G.token_ids(24, 1000)])
+    cuts = rng.integers(4096, 32768, 64)
+    reqs = [np.concatenate([sessions[i][:cuts[i]], G.token_ids(25, 500, seq_id=i)]) for i in range(64)]
+
+    def one(r):
+        h = K.kda_index_lookup(idx, r, pin=True)
+        if h["pin_handle"]:
+            K.kda_index_release(idx, h["pin_handle"])
+        return h
+    hl = one(req_long)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        one(req_long)
+    t_long = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for _ in range(reps // 10):
+        for r in reqs:
+            one(r)
+    t_short = (time.perf_counter() - t0) / (reps // 10 * len(reqs))
+    t0 = time.perf_counter()
+    for i, r in enumerate(reqs[:8]):
+        b = model.lookup(r)["boundary"]
+        # whole 6144-token pages match, then the deepest 4096-multiple checkpoint
+        assert b == K.kda_index_lookup(idx, r)["boundary"] == cuts[i] // pb * pb // 4096 * 4096
+    t_oracle = (time.perf_counter() - t0) / 8
+    assert hl["boundary"] == 900_000 // pb * pb
+    n_long = len(req_long)
+    return {"long_1m": {"tokens": n_long, "boundary": hl["boundary"], "pages": len(hl["pages"]),
+                        "ms_per_lookup": 1e3 * t_long,
+                        "hashed_gb_per_s": n_long * 4 / t_long / 1e9},
+            "sessions_32k": {"us_per_lookup": 1e6 * t_short, "lookups_per_s": 1.0 / t_short},
+            "oracle_32k_ms_per_lookup": 1e3 * t_oracle,
+            "entries": K.kda_index_stats(idx)[:2]}
+
+
 def cpu_baseline(G, w, d):
     """The fp64 oracle on the same 8K workload (all 32 heads, all tokens), timed on
     this host's cores.  Generation is excluded."""
@@ -526,6 +598,8 @@ def main():
         log(f"verify: {out['verify']}")
         out["short_conv"] = bench_conv(K, G)
         log(f"conv: {out['short_conv']}")
+        out["prefix_index"] = bench_index(K, G)
+        log(f"index: {out['prefix_index']}")
     if not args.only_prefill and not args.only_core:
         log("varlen resume: 16 sequences")
         out["varlen_resume"] = bench_varlen(K, G)

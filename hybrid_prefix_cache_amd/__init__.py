@@ -24,10 +24,12 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE = 0, 1, 2, 3
 KDA_ERR_PAGE_RANGE, KDA_ERR_PAGE_ALIAS, KDA_ERR_CKPT_ALIGN, KDA_ERR_CKPT_RANGE = 4, 5, 6, 7
 KDA_ERR_SEQ, KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_POOL = 8, 9, 10, 11
+KDA_ERR_PINNED, KDA_ERR_NOT_FOUND = 12, 13
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
                 4: "KDA_ERR_PAGE_RANGE", 5: "KDA_ERR_PAGE_ALIAS", 6: "KDA_ERR_CKPT_ALIGN",
                 7: "KDA_ERR_CKPT_RANGE", 8: "KDA_ERR_SEQ", 9: "KDA_ERR_WORKSPACE",
-                10: "KDA_ERR_HIP", 11: "KDA_ERR_POOL"}
+                10: "KDA_ERR_HIP", 11: "KDA_ERR_POOL", 12: "KDA_ERR_PINNED",
+                13: "KDA_ERR_NOT_FOUND"}
 KDA_F32, KDA_BF16 = 0, 1
 HASH_BLOCK = 512
 CHUNK = 64
@@ -37,7 +39,11 @@ EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset"
            "kda_decode_verify",
            "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
            "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8",
-           "kda_conv_workspace_bytes", "kda_short_conv", "kda_profile_enable", "kda_profile_read")
+           "kda_conv_workspace_bytes", "kda_short_conv", "kda_profile_enable", "kda_profile_read",
+           "kda_xxh64", "kda_chain_hashes", "kda_ckpt_plan", "kda_index_create",
+           "kda_index_destroy", "kda_index_register_pages", "kda_index_register_ckpt",
+           "kda_index_mark_ready", "kda_index_lookup", "kda_index_release", "kda_index_evict_page",
+           "kda_index_evict_ckpt", "kda_index_stats")
 
 
 class KdaError(RuntimeError):
@@ -56,6 +62,12 @@ class kda_conv_pool(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("page_bytes", ctypes.c_int64),
                 ("num_pages", ctypes.c_int32), ("channels", ctypes.c_int32),
                 ("width", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class kda_hit(ctypes.Structure):
+    _fields_ = [("boundary", ctypes.c_int64), ("mla_tokens", ctypes.c_int64),
+                ("num_pages", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("pin_handle", ctypes.c_int64)]
 
 
 class kda_kernel_stat(ctypes.Structure):
@@ -91,6 +103,20 @@ _sig = {
     "kda_conv_workspace_bytes": (_i64, [_i32, _i32]),
     "kda_short_conv": (ctypes.c_int, [ctypes.POINTER(kda_conv_pool), _P, _P, _P, ctypes.c_int, _i32,
                                       _P, _P, _P, _P, _P, _P, _P, _i32, _P, _sz, _P]),
+    "kda_xxh64": (ctypes.c_uint64, [_P, _i64, ctypes.c_uint64]),
+    "kda_chain_hashes": (_i64, [_P, _i64, _i32, ctypes.c_uint64, _P, _i64]),
+    "kda_ckpt_plan": (_i64, [_i64, _i64, _i32]),
+    "kda_index_create": (_P, [_i32, _i32, _i32, ctypes.c_uint64]),
+    "kda_index_destroy": (None, [_P]),
+    "kda_index_register_pages": (ctypes.c_int, [_P, _P, _i64, _P, _i32, _i64, _P]),
+    "kda_index_register_ckpt": (ctypes.c_int, [_P, _P, _i64, _i32, _i32, _i32, _i64, _P]),
+    "kda_index_mark_ready": (ctypes.c_int, [_P, _i64]),
+    "kda_index_lookup": (ctypes.c_int, [_P, _P, _i64, _i32, _P, _i32, _P,
+                                        ctypes.POINTER(kda_hit)]),
+    "kda_index_release": (ctypes.c_int, [_P, _i64]),
+    "kda_index_evict_page": (ctypes.c_int, [_P, _i32]),
+    "kda_index_evict_ckpt": (ctypes.c_int, [_P, _i32, _i32, _P]),
+    "kda_index_stats": (ctypes.c_int, [_P, _P, _P, _P]),
     "kda_profile_enable": (ctypes.c_int, [_i32]),
     "kda_profile_read": (_i32, [ctypes.POINTER(kda_kernel_stat), _i32, _i32]),
 }
@@ -297,6 +323,112 @@ def kda_short_conv(cpool, x, w, y, cu_seqlens, *, start_pos=None, state_in_page=
                              sp.ptr, si.ptr, so.ptr, ccu.ptr, cpos.ptr, cpg.ptr, hash_block,
                              _dptr(workspace), workspace_bytes, _stream(stream))
     _check(st)
+
+
+# ---- host prefix index (include/kda_index.h) --------------------------------
+def _tok(tokens):
+    return _HostArr(tokens, np.int32)
+
+
+def kda_xxh64(data: bytes, seed: int = 0) -> int:
+    buf = ctypes.create_string_buffer(bytes(data), len(data))
+    return int(_lib.kda_xxh64(buf, len(data), seed))
+
+
+def kda_chain_hashes(tokens, hash_block: int = HASH_BLOCK, seed: int = 0) -> np.ndarray:
+    t = _tok(tokens)
+    n = 0 if t.a is None else t.a.size
+    out = np.zeros(max(n // hash_block, 1), np.uint64)
+    got = _lib.kda_chain_hashes(t.ptr, n, hash_block, seed, out.ctypes.data, n // hash_block)
+    if got < 0:
+        raise ValueError("kda_chain_hashes: bad arguments")
+    return out[:got]
+
+
+def kda_ckpt_plan(start: int, length: int, hash_block: int = HASH_BLOCK) -> int:
+    return int(_lib.kda_ckpt_plan(start, length, hash_block))
+
+
+class PrefixIndex:
+    """Handle of a kda_index (pointer plus the shape the marshalling needs)."""
+
+    def __init__(self, ptr, hash_block, physical_block, num_groups):
+        self.ptr, self.hash_block, self.physical_block = ptr, hash_block, physical_block
+        self.num_groups = num_groups
+
+    def __del__(self, _destroy=_lib.kda_index_destroy):
+        if getattr(self, "ptr", None):
+            _destroy(self.ptr)
+            self.ptr = None
+
+
+def kda_index_create(hash_block: int = HASH_BLOCK, physical_block: int = 6144,
+                     num_groups: int = 1, namespace_seed: int = 0) -> PrefixIndex:
+    p = _lib.kda_index_create(hash_block, physical_block, num_groups, namespace_seed)
+    if not p:
+        raise KdaError(KDA_ERR_SHAPE, kda_last_error())
+    return PrefixIndex(p, hash_block, physical_block, num_groups)
+
+
+def kda_index_destroy(idx: PrefixIndex):
+    idx.__del__()
+
+
+def kda_index_register_pages(idx: PrefixIndex, tokens, pages, step: int = 0) -> np.ndarray:
+    t, pg = _tok(tokens), _HostArr(pages, np.int32)
+    n = 0 if t.a is None else t.a.size
+    npg = 0 if pg.a is None else pg.a.size
+    taken = np.zeros(max(npg, 1), np.int32)
+    _check(_lib.kda_index_register_pages(idx.ptr, t.ptr, n, pg.ptr, npg, step, taken.ctypes.data))
+    return taken[:npg]
+
+
+def kda_index_register_ckpt(idx: PrefixIndex, tokens, pos: int, group: int, page: int,
+                            durable: bool = False, step: int = 0) -> bool:
+    t = _tok(tokens)
+    taken = ctypes.c_int32(0)
+    _check(_lib.kda_index_register_ckpt(idx.ptr, t.ptr, pos, group, page, int(durable), step,
+                                        ctypes.byref(taken)))
+    return bool(taken.value)
+
+
+def kda_index_mark_ready(idx: PrefixIndex, step: int):
+    _check(_lib.kda_index_mark_ready(idx.ptr, step))
+
+
+def kda_index_lookup(idx: PrefixIndex, tokens, pin: bool = False, max_pages=None) -> dict:
+    t = _tok(tokens)
+    n = 0 if t.a is None else t.a.size
+    if max_pages is None:
+        max_pages = n // idx.physical_block + 1
+    pages = np.zeros(max(max_pages, 1), np.int32)
+    ck = np.zeros(idx.num_groups, np.int32)
+    hit = kda_hit()
+    _check(_lib.kda_index_lookup(idx.ptr, t.ptr, n, int(pin), pages.ctypes.data, max_pages,
+                                 ck.ctypes.data, ctypes.byref(hit)))
+    return {"boundary": hit.boundary, "mla_tokens": hit.mla_tokens,
+            "pages": pages[:hit.num_pages].tolist(), "ckpt_pages": ck.tolist(),
+            "pin_handle": hit.pin_handle}
+
+
+def kda_index_release(idx: PrefixIndex, pin_handle: int):
+    _check(_lib.kda_index_release(idx.ptr, pin_handle))
+
+
+def kda_index_evict_page(idx: PrefixIndex, page: int):
+    _check(_lib.kda_index_evict_page(idx.ptr, page))
+
+
+def kda_index_evict_ckpt(idx: PrefixIndex, group: int, page: int) -> list:
+    freed = np.zeros(idx.num_groups, np.int32)
+    _check(_lib.kda_index_evict_ckpt(idx.ptr, group, page, freed.ctypes.data))
+    return freed.tolist()
+
+
+def kda_index_stats(idx: PrefixIndex):
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.kda_index_stats(idx.ptr, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def kda_profile_enable(on: bool = True):

@@ -145,6 +145,12 @@ kda_status ship_metadata(uint8_t* ws, const std::vector<uint8_t>& blob, hipStrea
 
 }  // namespace
 
+namespace kda {
+// error text shared with the host-only translation units (the prefix index)
+void host_set_error(const char* msg) { g_err = msg; }
+void host_clear_error() { g_err.clear(); }
+}  // namespace kda
+
 extern "C" {
 
 int32_t kda_version(void) { return (1 << 16) | 0; }

@@ -75,7 +75,9 @@ typedef enum {
   KDA_ERR_SEQ = 8,         /* bad cu_seqlens / start_pos                          */
   KDA_ERR_WORKSPACE = 9,   /* workspace NULL, misaligned or too small             */
   KDA_ERR_HIP = 10,        /* a HIP launch or runtime call failed                 */
-  KDA_ERR_POOL = 11        /* invalid pool descriptor                             */
+  KDA_ERR_POOL = 11,       /* invalid pool descriptor                             */
+  KDA_ERR_PINNED = 12,     /* prefix index: eviction of an entry a lookup pinned   */
+  KDA_ERR_NOT_FOUND = 13   /* prefix index: no entry for that page / pin handle    */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;

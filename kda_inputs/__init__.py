@@ -35,7 +35,7 @@ DTYPES = {"f32": (F32, np.float32), "bf16": (BF16, np.uint16), "f64": (F64, np.f
 
 # stream ids (low 8 bits) per tensor; bits 8.. carry the sequence / request id
 TID_Q, TID_K, TID_V, TID_G, TID_BETA, TID_STATE, TID_PLAN = 1, 2, 3, 4, 5, 6, 7
-TID_CONV_X, TID_CONV_W = 8, 9
+TID_CONV_X, TID_CONV_W, TID_TOKENS = 8, 9, 10
 
 
 def build() -> str:
@@ -148,6 +148,12 @@ def conv_weights(seed, C, W):
     """Short-convolution taps, N(0, 1/W) fp32 -> float32 [C, W]."""
     return fill(seed, stream_id(TID_CONV_W), NORMAL, 0, C, 1, W, "f32",
                 scale=1.0 / np.sqrt(W)).reshape(C, W)
+
+
+def token_ids(seed, n, vocab=163_840, seq_id=0):
+    """n token ids, uniform over [0, vocab) (int32), for prefix-index workloads."""
+    u = uniforms(seed, stream_id(TID_TOKENS, seq_id), 0, n)
+    return np.minimum((u * vocab).astype(np.int64), vocab - 1).astype(np.int32)
 
 
 from .workloads import *  # noqa: E402,F401,F403
