@@ -766,8 +766,11 @@ __device__ __forceinline__ void load_ops_a(ChunkOps<D, Op, NH>& f, const ScanCtx
   using CO = ChunkOps<D, Op, NH>;
   using IO = InterOff<D>;
   const Op* pa = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kP : IO::kT);
+  // T and P are lower triangular: a row tile's fragments right of its
+  // diagonal block are zero and are neither loaded nor multiplied
 #pragma unroll
-  for (int i = 0; i < CO::NKC; ++i) f.fa[i] = frag_fm<Op>(pa, c.wv & 3, i, 64, c.lane);
+  for (int i = 0; i < CO::NKC; ++i)
+    if (i * CO::KK <= 16 * (c.wv & 3) + 15) f.fa[i] = frag_fm<Op>(pa, c.wv & 3, i, 64, c.lane);
 }
 
 template <int D, typename Op, int NH>
@@ -925,7 +928,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       for (int j = 0; j < NH; ++j) {
         f32x4 U = zero4(), X = zero4();
 #pragma unroll
-        for (int i = 0; i < CO::NKC; ++i) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 16 * j, i * KK, lane));
+        for (int i = 0; i < CO::NKC; ++i)
+          if (i * KK <= 16 * rt + 15) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 16 * j, i * KK, lane));
 #pragma unroll
         for (int i = 0; i < CO::NKD; ++i) mfma(X, cur.fb[i], frag<Op>(Sb, LDS_, 16 * j, i * KK, lane));
         Op* wdst = Wb + (16 * j + acc_col(lane)) * LDW + 16 * rt + acc_row(lane, 0);
@@ -941,7 +945,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       for (int j = 0; j < NH; ++j) {
         f32x4 OT4 = zero4();  // O^T[col = 16j + 4*(lane/16) + r][token = 16*rt + lane%16]
 #pragma unroll
-        for (int i = 0; i < CO::NKC; ++i) mfma(OT4, frag<Op>(Vb, LDW, 16 * j, i * KK, lane), cur.fa[i]);
+        for (int i = 0; i < CO::NKC; ++i)
+          if (i * KK <= 16 * rt + 15) mfma(OT4, frag<Op>(Vb, LDW, 16 * j, i * KK, lane), cur.fa[i]);
 #pragma unroll
         for (int i = 0; i < CO::NKD; ++i) mfma(OT4, frag<Op>(Sb, LDS_, 16 * j, i * KK, lane), cur.fb[i]);
         if (tok < len) {
