@@ -274,6 +274,8 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
     return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", workspace_bytes,
                 (long long)need);
   if ((int64_t)num_seqs * H > (int64_t)1 << 28) return fail(KDA_ERR_SHAPE, "too many (seq, head) pairs");
+  // the kernels address one 64-token chunk of q/k/v/g with 32-bit offsets
+  if ((int64_t)H * D > (int64_t)1 << 24) return fail(KDA_ERR_SHAPE, "num_heads * d_k above 2^24");
 
   // ---- metadata tables ------------------------------------------------------
   std::vector<uint8_t> blob((size_t)ml.inter_off, 0);

@@ -94,13 +94,29 @@ hipError_t launch_scan(int D, bool bf16, const ScanArgs& a, hipStream_t st);
 hipError_t launch_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t st);
 // Sequence owning a global chunk index: the largest s with
 // seqs[s].chunk_begin <= chunk (chunk tables are increasing).
-__device__ __forceinline__ int find_seq(const SeqEntry* seqs, int n, int chunk) {
+template <typename SeqPtr>
+__device__ __forceinline__ int find_seq(SeqPtr seqs, int n, int chunk) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
     if (seqs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+// The sequence table seen through the constant address space: uniform reads
+// of it are scalar loads even after the kernel has stored to global memory.
+typedef const __attribute__((address_space(4))) SeqEntry* ConstSeqPtr;
+__device__ __forceinline__ SeqEntry load_seq(ConstSeqPtr p, int i) {
+  SeqEntry e;
+  e.row_begin = p[i].row_begin;
+  e.start_pos = p[i].start_pos;
+  e.len = p[i].len;
+  e.chunk_begin = p[i].chunk_begin;
+  e.state_in = p[i].state_in;
+  e.state_out = p[i].state_out;
+  e.ckpt_begin = p[i].ckpt_begin;
+  e.ckpt_end = p[i].ckpt_end;
+  return e;
 }
 
 // One kda_short_conv call: 16-token blocks of the 64-token chunks of the

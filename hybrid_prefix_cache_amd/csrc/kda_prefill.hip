@@ -22,6 +22,7 @@
 // slab of S in fp32 registers.  Column j of S depends only on column j of v,
 // which is what allows the d_v split.  A partial final chunk is padded with
 // zero rows (k = q = v = g = beta = 0), which leave the state unchanged.
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -367,7 +368,7 @@ template <int D> struct Prep2Layout {
   static constexpr int TPP = 64 / TPARTS;      // tokens per run
   static constexpr int LDK = D + 8;            // [64][D] bf16 tiles
   static constexpr int LDC = 64 + 8;           // [*][64] bf16 tiles
-  static constexpr int LDF = 65;               // fp32 [64][65]
+  static constexpr int LDF = 68;               // fp32 [64][68] (16-byte rows)
   static constexpr int kTileK = 64 * LDK * 2;
   static constexpr int kRA = 0;
   static constexpr int kRABytes = (2 * kTileK > 2 * 64 * LDF * 4) ? 2 * kTileK : 2 * 64 * LDF * 4;
@@ -383,14 +384,84 @@ template <int D> struct Prep2Layout {
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
 
+template <int D> struct Prep2In {
+  static constexpr int TPP = Prep2Layout<D>::TPP;
+  // channel pair c0, c0+1 of tokens r0 .. r0+TPP-1, as loaded: rows at or past
+  // `len` hold a copy of the chunk's first row and are zeroed where consumed
+  // (selecting here would make the issuing thread wait for every load)
+  uint32_t k[TPP], q[TPP], g[TPP];
+  uint16_t beta;  // token t (threads t < 64), same convention
+  int len;        // valid rows of the chunk
+};
+
+// Element `off` (32-bit, in elements) of a uniform base pointer, so that the
+// access is addressed as scalar base + 32-bit vector offset.
+template <typename T>
+__device__ __forceinline__ T* at32(T* base, uint32_t off) {
+  using B = typename std::conditional<std::is_const<T>::value, const uint8_t, uint8_t>::type;
+  return reinterpret_cast<T*>(reinterpret_cast<B*>(base) + off * (uint32_t)sizeof(T));
+}
+
+// Global inputs of one (chunk, head) pair into registers: thread -> channel
+// pair cp, token run tp (4-byte loads, 256-byte coalesced per token).
+template <int D>
+__device__ __forceinline__ void prep2_load(const PrepArgs& a, int pair, int t, Prep2In<D>& x) {
+  using LY = Prep2Layout<D>;
+  constexpr int NP = LY::NP, TPP = LY::TPP;
+  // pair is uniform: the sequence table is read through the constant address
+  // space so that the lookup stays on the scalar unit (a vector load here
+  // would wait on every store still in flight; the table is not written
+  // while the kernel runs)
+  const int H = a.H;
+  const int chunk = __builtin_amdgcn_readfirstlane(pair / H);
+  const int h = __builtin_amdgcn_readfirstlane(pair - chunk * H);
+  const ConstSeqPtr cs = (ConstSeqPtr)(a.seqs);
+  const SeqEntry se = load_seq(cs, find_seq(cs, a.num_seqs, chunk));
+  const int lc = chunk - se.chunk_begin;
+  const int64_t row0 = se.row_begin + 64LL * lc;
+  const int len = min(64, se.len - 64 * lc);
+  const int c0 = 2 * (t % NP), r0 = (t / NP) * TPP;
+  // uniform row base, then 32-bit per-thread offsets (the host bounds
+  // 64 * H * D well below 2^31)
+  const int64_t rb = (row0 * H + h) * D;
+  const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.q) + rb;
+  const uint16_t* gk = reinterpret_cast<const uint16_t*>(a.k) + rb;
+  const uint16_t* gg = reinterpret_cast<const uint16_t*>(a.g) + rb;
+  const uint16_t* gb = reinterpret_cast<const uint16_t*>(a.beta) + row0 * H + h;
+  const uint32_t HD = (uint32_t)(H * D);
+#pragma unroll
+  for (int i = 0; i < TPP; ++i) {
+    const int r = r0 + i;
+    const uint32_t off = (r < len ? (uint32_t)r : 0u) * HD + (uint32_t)c0;
+    x.k[i] = *reinterpret_cast<const uint32_t*>(at32(gk, off));
+    x.q[i] = *reinterpret_cast<const uint32_t*>(at32(gq, off));
+    x.g[i] = *reinterpret_cast<const uint32_t*>(at32(gg, off));
+  }
+  const int tb = (t & 63) < len ? (t & 63) : 0;
+  x.beta = *at32(gb, (uint32_t)(tb * H));
+  x.len = len;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// low halves / high halves of two packed bf16 pairs: (a.lo, b.lo), (a.hi, b.hi)
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Persistent: the grid holds as many workgroups as fit on the device at once
+// and each walks the pairs with a stride of the grid size.  The kernel is
+// bound by instruction issue (one (chunk, head) pair is a few thousand vector
+// instructions per wave), so every phase is written to keep that count low:
+// wave-uniform control flow, 32-bit store offsets from a scalar base, results
+// produced in the orientation in which they are stored (4 or 8 contiguous
+// elements per lane), gates accumulated in base-2 units for v_exp_f32.
 template <int D>
 __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs) {
   using LY = Prep2Layout<D>;
   using IO = InterOff<D>;
   constexpr int NP = LY::NP, TPP = LY::TPP, LDK = LY::LDK, LDC = LY::LDC, LDF = LY::LDF;
+  constexpr float kLog2e = 1.4426950408889634f;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int t = threadIdx.x;
-  const int lane = t & 63, wv = t >> 6;
   uint8_t* base = smem;
   uint16_t* Kt = reinterpret_cast<uint16_t*>(base + LY::kRA);
   uint16_t* Kh = Kt + 64 * LDK;
@@ -408,86 +479,88 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
   // Pairs are taken in reverse order: the scan reads chunks first to last, so
   // the blocks written last (the earliest chunks) are the ones still resident
   // in the memory-side cache when it starts, instead of the ones evicted first.
-  const int pair = total_pairs - 1 - (int)blockIdx.x;
-  const int H = a.H;
-  const int chunk = pair / H, h = pair % H;
-  const SeqEntry se = a.seqs[find_seq(a.seqs, a.num_seqs, chunk)];
-  const int lc = chunk - se.chunk_begin;
-  const int64_t row0 = se.row_begin + 64LL * lc;
-  const int len = min(64, se.len - 64 * lc);
-  const uint16_t* gq = reinterpret_cast<const uint16_t*>(a.q);
-  const uint16_t* gk = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* gg = reinterpret_cast<const uint16_t*>(a.g);
-  const uint16_t* gb = reinterpret_cast<const uint16_t*>(a.beta);
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.inter + ((int64_t)chunk * H + h) * a.blk_bytes);
-
-  // ---- A: loads (thread -> channel pair cp, token run tp) -------------------
+  // The inputs of the next pair are loaded into registers once the current
+  // pair's have been consumed (after the decayed tiles), so their latency
+  // hides behind the Gram, inverse and product phases.
+  Prep2In<D> in;
+  if ((int)blockIdx.x < total_pairs) prep2_load<D>(a, total_pairs - 1 - (int)blockIdx.x, threadIdx.x, in);
+  for (int it = blockIdx.x; it < total_pairs; it += gridDim.x) {
+  // The thread index is made opaque per iteration so that the compiler derives
+  // the many per-thread LDS and global offsets inside the loop instead of
+  // hoisting them all out of it, which would keep them live in registers.
+  int t_opaque = threadIdx.x;
+  __asm__ volatile("" : "+v"(t_opaque));
+  const int t = t_opaque;
+  const int lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int cp = t % NP, tp = t / NP, c0 = 2 * cp, r0 = tp * TPP;
-  uint32_t gk2[TPP], gq2[TPP], gg2[TPP];
+  const int pair = total_pairs - 1 - it;
+  const int len = in.len;
+  if (len < 64) {  // rows past the chunk end read as zeros (uniform, rare)
 #pragma unroll
-  for (int i = 0; i < TPP; ++i) {
-    const int r = r0 + i;
-    const bool ok = r < len;
-    const int64_t off = ((row0 + (ok ? r : 0)) * H + h) * D + c0;
-    gk2[i] = ok ? *reinterpret_cast<const uint32_t*>(gk + off) : 0u;
-    gq2[i] = ok ? *reinterpret_cast<const uint32_t*>(gq + off) : 0u;
-    gg2[i] = ok ? *reinterpret_cast<const uint32_t*>(gg + off) : 0u;
+    for (int i = 0; i < TPP; ++i) {
+      const bool ok = r0 + i < len;
+      in.k[i] = ok ? in.k[i] : 0u;
+      in.q[i] = ok ? in.q[i] : 0u;
+      in.g[i] = ok ? in.g[i] : 0u;
+    }
   }
-  if (t < 64) beta_s[t] = t < len ? bf16_to_f32(gb[(row0 + t) * H + h]) : 0.f;
+  const int H = a.H;
+  const int chunk = pair / H, h = pair - (pair / H) * H;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.inter + ((int64_t)chunk * H + h) * a.blk_bytes);
+  if (it != (int)blockIdx.x) __syncthreads();  // the previous pair is done with LDS
+  if (t < 64) beta_s[t] = t < len ? bf16_to_f32(in.beta) : 0.f;
 
-  // ---- B: inclusive prefix sum of g over tokens (registers + run totals) ----
+  // ---- B: inclusive prefix sum of g * log2(e) over tokens --------------------
   float G0[TPP], G1[TPP];
   {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < TPP; ++i) {
-      s0 += bf16_to_f32((uint16_t)(gg2[i] & 0xffffu));
-      s1 += bf16_to_f32((uint16_t)(gg2[i] >> 16));
+      s0 = fmaf(bf_lo(in.g[i]), kLog2e, s0);
+      s1 = fmaf(bf_hi(in.g[i]), kLog2e, s1);
       G0[i] = s0;
       G1[i] = s1;
     }
-    partial[tp * D + c0] = s0;
-    partial[tp * D + c0 + 1] = s1;
+    *reinterpret_cast<float2*>(partial + tp * D + c0) = float2{s0, s1};
   }
   __syncthreads();
   float gc0 = 0.f, gc1 = 0.f, off0 = 0.f, off1 = 0.f;
 #pragma unroll
   for (int p = 0; p < LY::TPARTS; ++p) {
-    const float v0 = partial[p * D + c0], v1 = partial[p * D + c0 + 1];
-    if (p < tp) { off0 += v0; off1 += v1; }
-    gc0 += v0;
-    gc1 += v1;
+    const float2 v = *reinterpret_cast<const float2*>(partial + p * D + c0);
+    if (p < tp) { off0 += v.x; off1 += v.y; }
+    gc0 += v.x;
+    gc1 += v.y;
   }
   __syncthreads();  // partials are overwritten by Kt^T below
 
   // ---- C: decayed tiles --------------------------------------------------------
   {
-    const float eC0 = __expf(gc0), eC1 = __expf(gc1);
+    const float eC0 = __builtin_amdgcn_exp2f(gc0), eC1 = __builtin_amdgcn_exp2f(gc1);
     uint32_t ktT0[TPP / 2], ktT1[TPP / 2], ke0[TPP / 2], ke1[TPP / 2];
 #pragma unroll
-    for (int i = 0; i < TPP; ++i) {
-      const int r = r0 + i;
-      const float Ga = G0[i] + off0, Gb = G1[i] + off1;
-      const float e0 = __expf(Ga), e1 = __expf(Gb);
-      const float i0 = __expf(-Ga), i1 = __expf(-Gb);
-      const float k0 = bf16_to_f32((uint16_t)(gk2[i] & 0xffffu)), k1 = bf16_to_f32((uint16_t)(gk2[i] >> 16));
-      const float q0 = bf16_to_f32((uint16_t)(gq2[i] & 0xffffu)), q1 = bf16_to_f32((uint16_t)(gq2[i] >> 16));
-      const uint32_t kt = pack2(k0 * e0, k1 * e1);
-      *reinterpret_cast<uint32_t*>(Kt + r * LDK + c0) = kt;
-      *reinterpret_cast<uint32_t*>(Kh + r * LDK + c0) = pack2(k0 * i0, k1 * i1);
-      *reinterpret_cast<uint32_t*>(Qt + r * LDK + c0) = pack2(q0 * e0, q1 * e1);
-      const uint32_t ke = pack2(k0 * (eC0 * i0), k1 * (eC1 * i1));
-      if (i & 1) {
-        ktT0[i / 2] |= (kt & 0xffffu) << 16;
-        ktT1[i / 2] |= kt & 0xffff0000u;
-        ke0[i / 2] |= (ke & 0xffffu) << 16;
-        ke1[i / 2] |= ke & 0xffff0000u;
-      } else {
-        ktT0[i / 2] = kt & 0xffffu;
-        ktT1[i / 2] = kt >> 16;
-        ke0[i / 2] = ke & 0xffffu;
-        ke1[i / 2] = ke >> 16;
+    for (int i = 0; i < TPP; i += 2) {
+      uint32_t kt2[2], ke2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = r0 + i + u;
+        const float Ga = G0[i + u] + off0, Gb = G1[i + u] + off1;
+        const float e0 = __builtin_amdgcn_exp2f(Ga), e1 = __builtin_amdgcn_exp2f(Gb);
+        const float i0 = __builtin_amdgcn_exp2f(-Ga), i1 = __builtin_amdgcn_exp2f(-Gb);
+        const float k0 = bf_lo(in.k[i + u]), k1 = bf_hi(in.k[i + u]);
+        const float q0 = bf_lo(in.q[i + u]), q1 = bf_hi(in.q[i + u]);
+        const float kh0 = k0 * i0, kh1 = k1 * i1;
+        kt2[u] = pack_bf16x2(k0 * e0, k1 * e1);
+        ke2[u] = pack_bf16x2(kh0 * eC0, kh1 * eC1);
+        *reinterpret_cast<uint32_t*>(Kt + r * LDK + c0) = kt2[u];
+        *reinterpret_cast<uint32_t*>(Kh + r * LDK + c0) = pack_bf16x2(kh0, kh1);
+        *reinterpret_cast<uint32_t*>(Qt + r * LDK + c0) = pack_bf16x2(q0 * e0, q1 * e1);
       }
+      ktT0[i / 2] = lo_halves(kt2[0], kt2[1]);
+      ktT1[i / 2] = hi_halves(kt2[0], kt2[1]);
+      ke0[i / 2] = lo_halves(ke2[0], ke2[1]);
+      ke1[i / 2] = hi_halves(ke2[0], ke2[1]);
     }
     // token-contiguous runs: Kt^T rows c0, c0+1 in LDS; Kend^T rows in global
 #pragma unroll
@@ -496,58 +569,70 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
       const u32x4_t a1 = {ktT1[4 * v], ktT1[4 * v + 1], ktT1[4 * v + 2], ktT1[4 * v + 3]};
       *reinterpret_cast<u32x4_t*>(KtT + c0 * LDC + r0 + 8 * v) = a0;
       *reinterpret_cast<u32x4_t*>(KtT + (c0 + 1) * LDC + r0 + 8 * v) = a1;
-      {
-        const u32x4_t b0 = {ke0[4 * v], ke0[4 * v + 1], ke0[4 * v + 2], ke0[4 * v + 3]};
-        const u32x4_t b1 = {ke1[4 * v], ke1[4 * v + 1], ke1[4 * v + 2], ke1[4 * v + 3]};
-        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + frag_off<32>(c0, r0 + 8 * v, 64)) = b0;
-        *reinterpret_cast<u32x4_t*>(out + IO::kKendT + frag_off<32>(c0 + 1, r0 + 8 * v, 64)) = b1;
-      }
+      const u32x4_t b0 = {ke0[4 * v], ke0[4 * v + 1], ke0[4 * v + 2], ke0[4 * v + 3]};
+      const u32x4_t b1 = {ke1[4 * v], ke1[4 * v + 1], ke1[4 * v + 2], ke1[4 * v + 3]};
+      *reinterpret_cast<u32x4_t*>(at32(out, IO::kKendT + frag_off<32>(c0, r0 + 8 * v, 64))) = b0;
+      *reinterpret_cast<u32x4_t*>(at32(out, IO::kKendT + frag_off<32>(c0 + 1, r0 + 8 * v, 64))) = b1;
     }
-    if (tp == 0) {
-      float* gamma = reinterpret_cast<float*>(out + IO::kGammaElems);
-      gamma[c0] = eC0;
-      gamma[c0 + 1] = eC1;
-    }
+    if (tp == 0)
+      *reinterpret_cast<float2*>(at32(reinterpret_cast<float*>(out + IO::kGammaElems), c0)) = float2{eC0, eC1};
   }
+  // this pair's inputs are consumed: load the next pair's into the same
+  // registers (beta has been staged in LDS at the top of the iteration)
+  if (it + (int)gridDim.x < total_pairs) prep2_load<D>(a, pair - (int)gridDim.x, t, in);
   __syncthreads();
 
-  // ---- D: Gram matrices (waves 0,1: Kt Kh^T; waves 2,3: Qt Kh^T) --------------
-  // each wave takes block rows {0,3} or {1,2}; a row's A fragments are loaded
-  // once and reused for every tile of the row
+  // ---- D: Gram matrices, formed transposed (M = key token j, N = token i) ---
+  // so that a lane holds 4 consecutive columns j of one row i.  Waves 0,1:
+  // A = Kt Kh^T -> L = diag(beta) strictLower(A) (fp32); waves 2,3:
+  // Aq = lowerIncl(Qt Kh^T) (bf16).  Each wave takes row blocks {0,3} or
+  // {1,2} (5 lower tiles, 3 upper tiles written as zeros for Aq).
   {
     const int gram = wv >> 1;
-    const uint16_t* Aop = gram == 0 ? Kt : Qt;
+    const uint16_t* Bop = gram == 0 ? Kt : Qt;
     constexpr int NKD = D / 32;
     f32x4 acc[2][4];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      const int mt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
-      Frag<uint16_t> af[NKD];
+      const int nt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);  // row block of i
+      Frag<uint16_t> bf[NKD];
 #pragma unroll
-      for (int i = 0; i < NKD; ++i) af[i] = frag<uint16_t>(Aop, LDK, 16 * mt, 32 * i, lane);
+      for (int k = 0; k < NKD; ++k) bf[k] = frag<uint16_t>(Bop, LDK, 16 * nt, 32 * k, lane);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        acc[pass][nt] = zero4();
-        if (nt <= mt) {
+      for (int mt = 0; mt < 4; ++mt) {  // column block of j
+        acc[pass][mt] = zero4();
+        if (mt <= nt) {
 #pragma unroll
-          for (int i = 0; i < NKD; ++i) mfma(acc[pass][nt], af[i], frag<uint16_t>(Kh, LDK, 16 * nt, 32 * i, lane));
+          for (int k = 0; k < NKD; ++k) mfma(acc[pass][mt], frag<uint16_t>(Kh, LDK, 16 * mt, 32 * k, lane), bf[k]);
         }
       }
     }
     __syncthreads();  // Kt/Kh are overwritten by L below
+    const int jq = 4 * (lane >> 4);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      const int mt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
+      const int nt = (wv & 1) ? (pass ? 2 : 1) : (pass ? 3 : 0);
+      const int i = 16 * nt + (lane & 15);
+      if (gram == 0) {
+        const float bi = beta_s[i];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+        for (int mt = 0; mt < 4; ++mt) {
+          if (mt <= nt) {
+            const int j0 = 16 * mt + jq;
+            f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-          if (gram == 0) {
-            if (nt <= mt) Lm[i * LDF + j] = (j < i) ? beta_s[i] * acc[pass][nt][r] : 0.f;
-          } else {
-            Aq[i * LDC + j] = f32_to_bf16((j <= i) ? acc[pass][nt][r] : 0.f);
+            for (int r = 0; r < 4; ++r) v[r] = (j0 + r < i) ? bi * acc[pass][mt][r] : 0.f;
+            *reinterpret_cast<f32x4*>(Lm + i * LDF + j0) = v;
           }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int j0 = 16 * mt + jq;
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (j0 + r <= i) ? acc[pass][mt][r] : 0.f;
+          *reinterpret_cast<u16x4*>(Aq + i * LDC + j0) = pack_bf16x4(v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -606,53 +691,67 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
   }
   __syncthreads();
   {
-    // T[i][j] = Tinv[i][j] beta_j (j <= i); thread t owns column j = t & 63,
-    // rows i = (t >> 6) + 4 q
-    const int j = t & 63;
-    const float bj = beta_s[j];
-    float tv[16];
+    // T[i][j] = Tinv[i][j] beta_j (j <= i), as bf16, in both orientations:
+    //   row view:    thread -> row i = t / 4, columns 16 (t % 4) .. + 15
+    //   column view: thread -> column j = t / 4, rows 16 (t % 4) .. + 15
+    // Each thread reads its 16 + 16 values before the barrier (T overwrites
+    // Tinv), then writes two 32-byte runs per view; the row view also goes to
+    // global memory (fragment-major, 16-byte runs of 8 columns).
+    const int rv = t >> 2, g16 = 16 * (t & 3);
+    uint32_t rowp[8], colp[8];
+    {
+      const float* src = Ti + rv * LDF + g16;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int i = (t >> 6) + 4 * q;
-      tv[q] = (j <= i) ? Ti[i * LDF + j] * bj : 0.f;
+      for (int m = 0; m < 16; m += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + m);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(beta_s + g16 + m);
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = (g16 + m + r <= rv) ? x[r] * b[r] : 0.f;
+        rowp[m / 2] = pack_bf16x2(y[0], y[1]);
+        rowp[m / 2 + 1] = pack_bf16x2(y[2], y[3]);
+      }
+      const float bj = beta_s[rv];
+#pragma unroll
+      for (int m = 0; m < 16; m += 2) {
+        const int i = g16 + m;
+        const float y0 = (rv <= i) ? Ti[i * LDF + rv] * bj : 0.f;
+        const float y1 = (rv <= i + 1) ? Ti[(i + 1) * LDF + rv] * bj : 0.f;
+        colp[m / 2] = pack_bf16x2(y0, y1);
+      }
     }
     __syncthreads();  // Tinv is overwritten by T / T^T below
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int i = (t >> 6) + 4 * q;
-      const uint16_t v = f32_to_bf16(tv[q]);
-      Tb[i * LDC + j] = v;
-      TbT[j * LDC + i] = v;
-    }
+    uint16_t* tr = Tb + rv * LDC + g16;
+    uint16_t* tc = TbT + rv * LDC + g16;
+    const u32x4_t r0v = {rowp[0], rowp[1], rowp[2], rowp[3]}, r1v = {rowp[4], rowp[5], rowp[6], rowp[7]};
+    *reinterpret_cast<u32x4_t*>(tr) = r0v;
+    *reinterpret_cast<u32x4_t*>(tr + 8) = r1v;
+    *reinterpret_cast<u32x4_t*>(tc) = u32x4_t{colp[0], colp[1], colp[2], colp[3]};
+    *reinterpret_cast<u32x4_t*>(tc + 8) = u32x4_t{colp[4], colp[5], colp[6], colp[7]};
+    *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16, 64))) = r0v;
+    *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16 + 8, 64))) = r1v;
   }
   __syncthreads();
-  {  // T to global in fragment-major order: 16-byte runs of 8 columns
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int cidx = t + 256 * q, i = cidx >> 3, j0 = (cidx & 7) * 8;
-      *reinterpret_cast<u16x8*>(out + IO::kT + frag_off<32>(i, j0, 64)) =
-          *reinterpret_cast<const u16x8*>(Tb + i * LDC + j0);
-    }
-  }
 
-  // ---- F: Keff^T = Kt^T T^T  (M = channels, N = tokens; T lower triangular) ---
+  // ---- F: Keff = T Kt.  Formed twice: transposed (M = channels) for the
+  // global copy, whose fragments hold 8 consecutive channels of a token, and
+  // direct (M = tokens) for the LDS copy Keff^T, which needs runs of tokens.
+  // T is lower triangular: tokens of row blocks 0, 1 only need k < 32.
   constexpr int MTW = D / 64;  // channel tiles per wave
-  f32x4 kacc[MTW][4];
+  f32x4 kd[MTW][4];
 #pragma unroll
   for (int u = 0; u < MTW; ++u) {
     const int mt = MTW * wv + u;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      kacc[u][nt] = zero4();
       const int ke = nt < 2 ? 32 : 64;
-      tile_mma<uint16_t>(kacc[u][nt], KtT, LDC, 16 * mt, Tb, LDC, 16 * nt, 0, ke, lane);
-      {  // Keff[tok][ch .. ch+3]: lane holds 4 consecutive channels of one token
-        const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
-        u16x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(kacc[u][nt][r]);
-        *reinterpret_cast<u16x4*>(out + IO::kKeff + frag_off<32>(tok, ch, D)) = w;
-      }
+      f32x4 acc = zero4();
+      tile_mma<uint16_t>(acc, KtT, LDC, 16 * mt, Tb, LDC, 16 * nt, 0, ke, lane);
+      const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
+      *reinterpret_cast<u16x4*>(at32(out, IO::kKeff + frag_off<32>(tok, ch, D))) =
+          pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
+      kd[u][nt] = zero4();
+      tile_mma<uint16_t>(kd[u][nt], Tb, LDC, 16 * nt, KtT, LDC, 16 * mt, 0, ke, lane);
     }
   }
   __syncthreads();  // Kt^T is overwritten by Keff^T below
@@ -661,9 +760,8 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
     const int mt = MTW * wv + u;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        KeffT[(16 * mt + acc_row(lane, r)) * LDC + 16 * nt + acc_col(lane)] = f32_to_bf16(kacc[u][nt][r]);
+      *reinterpret_cast<u16x4*>(KeffT + (16 * mt + acc_col(lane)) * LDC + 16 * nt + acc_row(lane, 0)) =
+          pack_bf16x4(kd[u][nt][0], kd[u][nt][1], kd[u][nt][2], kd[u][nt][3]);
   }
   __syncthreads();
 
@@ -676,14 +774,11 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
       f32x4 acc = zero4();
       const int ke = nt < 2 ? 32 : 64;
       tile_mma<uint16_t>(acc, KeffT, LDC, 16 * mt, Aq, LDC, 16 * nt, 0, ke, lane);
-      {
-        const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
-        const u16x4 qv = *reinterpret_cast<const u16x4*>(Qt + tok * LDK + ch);
-        u16x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(bf16_to_f32(qv[r]) - acc[r]);
-        *reinterpret_cast<u16x4*>(out + IO::kQeff + frag_off<32>(tok, ch, D)) = w;
-      }
+      const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
+      const u16x4 qv = *reinterpret_cast<const u16x4*>(Qt + tok * LDK + ch);
+      *reinterpret_cast<u16x4*>(at32(out, IO::kQeff + frag_off<32>(tok, ch, D))) =
+          pack_bf16x4(bf16_to_f32(qv[0]) - acc[0], bf16_to_f32(qv[1]) - acc[1],
+                      bf16_to_f32(qv[2]) - acc[2], bf16_to_f32(qv[3]) - acc[3]);
     }
   }
   {
@@ -696,14 +791,11 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
         const int kb = (16 * mt) / 32 * 32, ke = nt < 2 ? 32 : 64;
         tile_mma<uint16_t>(acc, TbT, LDC, 16 * mt, Aq, LDC, 16 * nt, kb, ke, lane);
       }
-      {
-        const int tok = 16 * nt + acc_col(lane), col = 16 * mt + acc_row(lane, 0);
-        u16x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = f32_to_bf16(acc[r]);
-        *reinterpret_cast<u16x4*>(out + IO::kP + frag_off<32>(tok, col, 64)) = w;
-      }
+      const int tok = 16 * nt + acc_col(lane), col = 16 * mt + acc_row(lane, 0);
+      *reinterpret_cast<u16x4*>(at32(out, IO::kP + frag_off<32>(tok, col, 64))) =
+          pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
     }
+  }
   }
 }
 
@@ -1029,13 +1121,29 @@ static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D>
 static hipError_t launch_prep2_t(const PrepArgs& a, int total_chunks, hipStream_t st) {
   constexpr int kBytes = Prep2Layout<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prep2_kernel<D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
   const int pairs = total_chunks * a.H;
-  hipLaunchKernelGGL((prep2_kernel<D>), dim3(pairs), dim3(256), kBytes, st, a, pairs);
+  // two workgroups per CU fit (LDS); one grid-sized wave of them walks all pairs
+  const int grid = (int)std::min<int64_t>(pairs, 2LL * device_cu_count());
+  hipLaunchKernelGGL((prep2_kernel<D>), dim3(grid), dim3(256), kBytes, st, a, pairs);
   return hipGetLastError();
 }
 
