@@ -106,6 +106,9 @@ __device__ __forceinline__ int find_seq(SeqPtr seqs, int n, int chunk) {
 // The sequence table seen through the constant address space: uniform reads
 // of it are scalar loads even after the kernel has stored to global memory.
 typedef const __attribute__((address_space(4))) SeqEntry* ConstSeqPtr;
+// The checkpoint table through the constant address space (scalar loads).
+typedef const __attribute__((address_space(4))) CkptEntry* ConstCkptPtr;
+
 __device__ __forceinline__ SeqEntry load_seq(ConstSeqPtr p, int i) {
   SeqEntry e;
   e.row_begin = p[i].row_begin;

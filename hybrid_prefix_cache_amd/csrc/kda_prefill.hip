@@ -913,6 +913,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   using CO = ChunkOps<D, Op, NH>;
   constexpr int BW = 16 * NH, NS = D / BW, KK = OT::kK;
   constexpr int PF = sizeof(Op) == 2 ? 3 : 1;  // chunks of operands prefetched ahead
+  // bf16: the few LDS operand fragments of a product are read up front (fp32
+  // has 8x as many fragments; they are read as the products go)
+  constexpr bool kBatchLds = sizeof(Op) == 2;
   constexpr int PAD = 16 / (int)sizeof(Op);
   constexpr int LDS_ = D + PAD, LDW = 64 + PAD;
   __shared__ __align__(16) Op Sb[BW * LDS_];  // S^T slab [col][row]
@@ -925,7 +928,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   if (p >= a.npairs) return;
   const int H = a.H, h = p % H;
   const SeqEntry se = a.seqs[a.order[p / H]];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches per role
   ScanCtx c;
   c.inter = a.inter;
   c.blk_bytes = a.blk_bytes;
@@ -990,7 +994,10 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   s_to_lds();
 
   int nck = se.ckpt_begin;
-  int64_t next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
+  // read through the constant address space: a vector load here would wait
+  // for every operand load in flight
+  const ConstCkptPtr ck = (ConstCkptPtr)(a.ckpts);
+  int64_t next_pos = nck < se.ckpt_end ? ck[nck].pos : -1;
 
   auto step = [&](CO& cur, CO& pre, int n) {
     const int nf = min(n + PF, nchunks - 1);  // chunk whose operands are prefetched
@@ -1015,32 +1022,68 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
     load_ops_b<D, Op, NH>(pre, c, nf);
     __builtin_amdgcn_sched_barrier(0);
 
+    // Each product reads its LDS operands (V^T and the bf16 copy of S) into
+    // registers before the first MFMA, and accumulates in independent halves
+    // that are summed at the end: the chains are then as short as the
+    // matrix-core dependency allows instead of one LDS round trip per MFMA.
     if (!c.is_o) {
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        f32x4 U = zero4(), X = zero4();
+        f32x4 U = zero4(), X0 = zero4(), X1 = zero4();
+        if constexpr (kBatchLds) {
+          Frag<Op> vf[CO::NKC], sf[CO::NKD];
 #pragma unroll
-        for (int i = 0; i < CO::NKC; ++i)
-          if (i * KK <= 16 * rt + 15) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 16 * j, i * KK, lane));
+          for (int i = 0; i < CO::NKC; ++i)
+            if (i * KK <= 16 * rt + 15) vf[i] = frag<Op>(Vb, LDW, 16 * j, i * KK, lane);
 #pragma unroll
-        for (int i = 0; i < CO::NKD; ++i) mfma(X, cur.fb[i], frag<Op>(Sb, LDS_, 16 * j, i * KK, lane));
+          for (int i = 0; i < CO::NKD; ++i) sf[i] = frag<Op>(Sb, LDS_, 16 * j, i * KK, lane);
+#pragma unroll
+          for (int i = 0; i < CO::NKC; ++i)
+            if (i * KK <= 16 * rt + 15) mfma(U, cur.fa[i], vf[i]);
+#pragma unroll
+          for (int i = 0; i < CO::NKD; ++i) mfma(i < CO::NKD / 2 ? X0 : X1, cur.fb[i], sf[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CO::NKC; ++i)
+            if (i * KK <= 16 * rt + 15) mfma(U, cur.fa[i], frag<Op>(Vb, LDW, 16 * j, i * KK, lane));
+#pragma unroll
+          for (int i = 0; i < CO::NKD; ++i)
+            mfma(i < CO::NKD / 2 ? X0 : X1, cur.fb[i], frag<Op>(Sb, LDS_, 16 * j, i * KK, lane));
+        }
+        const f32x4 Wv = U - X0 - X1;
         Op* wdst = Wb + (16 * j + acc_col(lane)) * LDW + 16 * rt + acc_row(lane, 0);
         if constexpr (sizeof(Op) == 2)
-          *reinterpret_cast<u16x4*>(wdst) =
-              pack_bf16x4(U[0] - X[0], U[1] - X[1], U[2] - X[2], U[3] - X[3]);
+          *reinterpret_cast<u16x4*>(wdst) = pack_bf16x4(Wv[0], Wv[1], Wv[2], Wv[3]);
         else
-          *reinterpret_cast<f32x4*>(wdst) = U - X;
+          *reinterpret_cast<f32x4*>(wdst) = Wv;
       }
     } else {
       const int tok = 16 * rt + acc_col(lane);
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        f32x4 OT4 = zero4();  // O^T[col = 16j + 4*(lane/16) + r][token = 16*rt + lane%16]
+        // O^T[col = 16j + 4*(lane/16) + r][token = 16*rt + lane%16]
+        f32x4 OA = zero4(), OB0 = zero4(), OB1 = zero4();
+        if constexpr (kBatchLds) {
+          Frag<Op> vf[CO::NKC], sf[CO::NKD];
 #pragma unroll
-        for (int i = 0; i < CO::NKC; ++i)
-          if (i * KK <= 16 * rt + 15) mfma(OT4, frag<Op>(Vb, LDW, 16 * j, i * KK, lane), cur.fa[i]);
+          for (int i = 0; i < CO::NKC; ++i)
+            if (i * KK <= 16 * rt + 15) vf[i] = frag<Op>(Vb, LDW, 16 * j, i * KK, lane);
 #pragma unroll
-        for (int i = 0; i < CO::NKD; ++i) mfma(OT4, frag<Op>(Sb, LDS_, 16 * j, i * KK, lane), cur.fb[i]);
+          for (int i = 0; i < CO::NKD; ++i) sf[i] = frag<Op>(Sb, LDS_, 16 * j, i * KK, lane);
+#pragma unroll
+          for (int i = 0; i < CO::NKC; ++i)
+            if (i * KK <= 16 * rt + 15) mfma(OA, vf[i], cur.fa[i]);
+#pragma unroll
+          for (int i = 0; i < CO::NKD; ++i) mfma(i < CO::NKD / 2 ? OB0 : OB1, sf[i], cur.fb[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CO::NKC; ++i)
+            if (i * KK <= 16 * rt + 15) mfma(OA, frag<Op>(Vb, LDW, 16 * j, i * KK, lane), cur.fa[i]);
+#pragma unroll
+          for (int i = 0; i < CO::NKD; ++i)
+            mfma(i < CO::NKD / 2 ? OB0 : OB1, frag<Op>(Sb, LDS_, 16 * j, i * KK, lane), cur.fb[i]);
+        }
+        const f32x4 OT4 = OA + OB0 + OB1;
         if (tok < len) {
           const int64_t base =
               ((c.row_begin + 64LL * n + tok) * H + h) * D + c.c0 + 16 * j + acc_row(lane, 0);
@@ -1065,9 +1108,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       }
     }
     if (se.start_pos + 64LL * n + len == next_pos) {
-      s_store(a.ckpts[nck].page);
+      s_store(ck[nck].page);
       ++nck;
-      next_pos = nck < se.ckpt_end ? a.ckpts[nck].pos : -1;
+      next_pos = nck < se.ckpt_end ? ck[nck].pos : -1;
     }
     s_to_lds();
   };
