@@ -10,12 +10,13 @@
 //
 // Per head of a compressed page: int8 q[d][d] (row i = d_k index), then fp32
 // scale[d]; scale_i = max_j |S_ij| / 127, q_ij = clamp(rne(S_ij / scale_i),
-// -127, 127) (0 when scale_i == 0), restore S~_ij = q_ij * scale_i.  Division is
-// the IEEE fp32 division (the compiler's correctly rounded sequence), so the
-// codes are a fixed function of the fp32 state.
+// -127, 127) (0 when scale_i == 0), restore S~_ij = q_ij * scale_i.  The
+// quotient is the IEEE fp32 division, so the codes are a fixed function of the
+// fp32 state; the kernel reaches the same codes with a reciprocal multiply and
+// falls back to the division only where the two could round differently.
 //
 // A 256-thread workgroup covers 256 / (d/4) rows of one head per pass: each
-// thread holds one 16-byte vector of a row, the row max-abs is a shuffle
+// thread holds one 16-byte vector of a row, the row max-abs is a DPP
 // reduction over the d/4 lanes of the row, and each thread writes its 4 codes
 // as one 4-byte store (a row of codes is one 128-byte line at d = 128).  Both
 // directions are HBM streams; state accesses are non-temporal.  The write is
@@ -41,6 +42,46 @@ __device__ __forceinline__ uint32_t code_of(float x, float scale) {
   return (uint32_t)(uint8_t)(int8_t)(int)r;
 }
 
+// The same code with one multiply instead of a division.  q = x * rcp(scale)
+// differs from the correctly rounded quotient RN(x / scale) by less than
+// 3e-5 for |x / scale| <= 127 (v_rcp_f32 is within 1 ulp, the product adds half
+// an ulp, RN(x / scale) half an ulp), and round-to-nearest-even changes value
+// only at half-integers; so when the fraction of q is more than 2^-14 away
+// from 1/2 both quotients round to the same integer.  `amb` is set otherwise
+// (about one element in 8,000, and for scale 0 or non-finite, where q is NaN);
+// the caller then recomputes the row's codes with the division.
+__device__ __forceinline__ uint32_t code_fast(float x, float inv, bool& amb) {
+  const float q = x * inv;
+  amb |= !(fabsf(__builtin_amdgcn_fractf(q) - 0.5f) > 0x1p-14f);
+  const float r = __builtin_amdgcn_fmed3f(rintf(q), -127.f, 127.f);
+  return (uint32_t)(uint8_t)(int8_t)(int)r;
+}
+
+// RN(m / 127) without a division: q1 = m * RN(1/127), then one correction
+// step with the exact remainder fma(-q1, 127, m).  Checked equal to the IEEE
+// quotient for every non-negative finite fp32 m (all 2^31 - 2^23 of them,
+// denormals included) by an exhaustive host-side comparison.
+__device__ __forceinline__ float div127(float m) {
+  constexpr float kR = 1.0f / 127.0f;
+  const float q1 = m * kR;
+  const float e = __builtin_fmaf(-q1, 127.0f, m);
+  return __builtin_fmaf(e, kR, q1);
+}
+
+// Maximum over the LPR lanes that hold one row (LPR = 16 or 32, aligned):
+// rotations by 1, 2, 4, 8 inside each 16-lane DPP row, then one exchange with
+// the other half for 32-lane rows.
+template <int LPR>
+__device__ __forceinline__ uint32_t row_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));  // row_ror:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));  // row_ror:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  if constexpr (LPR == 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  static_assert(LPR == 16 || LPR == 32, "rows of 16 or 32 lanes");
+  return v;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   using QS = QuantShape<D>;
@@ -60,12 +101,19 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     const int row = row0 + k * QS::RPW;
-    float m = fmaxf(fmaxf(fabsf(x[k].x), fabsf(x[k].y)), fmaxf(fabsf(x[k].z), fabsf(x[k].w)));
-#pragma unroll
-    for (int o = QS::LPR / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));  // the row's lanes
-    const float scale = m / 127.f;
-    const uint32_t packed = code_of(x[k].x, scale) | (code_of(x[k].y, scale) << 8) |
-                            (code_of(x[k].z, scale) << 16) | (code_of(x[k].w, scale) << 24);
+    // max |x| over the row: on the magnitude bit patterns, whose unsigned order
+    // is the order of the magnitudes (a NaN compares above everything)
+    uint32_t mu = max(max(__float_as_uint(x[k].x) & 0x7fffffffu, __float_as_uint(x[k].y) & 0x7fffffffu),
+                      max(__float_as_uint(x[k].z) & 0x7fffffffu, __float_as_uint(x[k].w) & 0x7fffffffu));
+    const float m = __uint_as_float(row_max<QS::LPR>(mu));
+    const float scale = div127(m);  // m / 127, correctly rounded
+    const float inv = __builtin_amdgcn_rcpf(scale);
+    bool amb = false;
+    uint32_t packed = code_fast(x[k].x, inv, amb) | (code_fast(x[k].y, inv, amb) << 8) |
+                      (code_fast(x[k].z, inv, amb) << 16) | (code_fast(x[k].w, inv, amb) << 24);
+    if (__builtin_expect(amb, 0))
+      packed = code_of(x[k].x, scale) | (code_of(x[k].y, scale) << 8) | (code_of(x[k].z, scale) << 16) |
+               (code_of(x[k].w, scale) << 24);
     *reinterpret_cast<uint32_t*>(qh + row * D + c) = packed;
     if (threadIdx.x % QS::LPR == 0) *reinterpret_cast<float*>(qh + (int64_t)D * D + 4 * row) = scale;
   }

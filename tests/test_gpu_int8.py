@@ -116,3 +116,48 @@ def test_resume_through_int8_checkpoint():
     err_o = max(rel_fro(got[:, h], ref["o"][:, h]) for h in range(H))
     err_s = max(rel_fro(pb.states(2)[h], ref["s_final"][0, h]) for h in range(H))
     assert err_o <= 2e-2 and err_s <= 2e-2, (err_o, err_s)
+
+
+def _tie_states(seed, H, D):
+    """Rows built so that most quotients x / scale land on a half-integer or
+    one ulp beside one (where a reciprocal multiply and the IEEE division could
+    round differently), with denormal, power-of-two and constant rows."""
+    rng = np.random.default_rng(seed)
+    s = np.empty((H, D, D), np.float32)
+    for h in range(H):
+        for i in range(D):
+            kind = (h * D + i) % 5
+            m = np.float32(2.0 ** int(rng.integers(-20, 20)) * rng.uniform(1, 2))
+            if kind == 3:
+                m = np.float32(2.0 ** int(rng.integers(-10, 10)))
+            if kind == 4:
+                m = np.float32(1e-40 * (1 + i))           # denormal row maximum
+            scale = np.float32(m / np.float32(127.0))
+            ks = rng.integers(-126, 126, D).astype(np.float64) + 0.5
+            x = (ks * np.float64(scale)).astype(np.float32)
+            nud = rng.integers(-1, 2, D)
+            x = np.where(nud > 0, np.nextafter(x, np.float32(np.inf)),
+                         np.where(nud < 0, np.nextafter(x, np.float32(-np.inf)), x)).astype(np.float32)
+            x = np.clip(x, -m, m).astype(np.float32)
+            x[0] = -m if kind == 2 else m
+            if kind == 2 and i % 2:
+                x[:] = -m                                   # every element at the maximum
+            s[h, i] = x
+    return s
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_write_bitexact_at_rounding_ties(D):
+    """Codes and scales bit-exact where the quotient sits on or next to a
+    rounding boundary, for denormal and power-of-two scales too."""
+    H = 2
+    s = _tie_states(7 + D, H, D)
+    pb = PoolBuf(1, H, D)
+    pb.set_states(0, s)
+    qp = QPool(1, H, D)
+    K.kda_checkpoint_write_int8(pb.pool, [0], qp.pool, [0])
+    torch.cuda.synchronize()
+    q, sc = quant.quantize(s)
+    ties = np.abs(np.abs(np.float32(s) / np.where(sc > 0, sc, 1)[..., None]) % 1 - 0.5) < 1e-5
+    assert ties.mean() > 0.2  # the rows do exercise the boundary
+    assert np.array_equal(qp.page(0)[:H * qp.head_bytes], quant.pack_page(q, sc))
