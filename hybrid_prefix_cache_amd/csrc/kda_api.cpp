@@ -308,12 +308,25 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
   // ---- launches --------------------------------------------------------------
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  s = ship_metadata(ws, blob, st);
-  if (s != KDA_OK) return s;
+  // small tables travel inside the kernel arguments (no fill launch)
+  const bool inl = num_seqs <= kInlineSeqs && num_ckpts <= kInlineCkpts;
+  if (!inl) {
+    s = ship_metadata(ws, blob, st);
+    if (s != KDA_OK) return s;
+  }
+  InlineSeqs iseq;
+  InlineCkpts ick;
+  std::memset(&iseq, 0, sizeof(iseq));
+  std::memset(&ick, 0, sizeof(ick));
+  if (inl) {
+    std::memcpy(iseq.e, seqs, sizeof(SeqEntry) * num_seqs);
+    std::memcpy(iseq.order, order.data(), sizeof(int32_t) * num_seqs);
+    std::memcpy(ick.e, ck, sizeof(CkptEntry) * num_ckpts);
+  }
   uint8_t* inter = ws + ml.inter_off;
   if (total_chunks > 0) {
     PrepArgs pa{q, k, g, beta, reinterpret_cast<const SeqEntry*>(ws + ml.seq_off), num_seqs, H,
-                inter, blk};
+                inter, blk, inl ? 1 : 0, 0, iseq};
     Launch L("kda_prefill_prep", st);
     hipError_t e = launch_prep(D, bf, pa, (int)total_chunks, st);
     if (e != hipSuccess) return hip_fail(e, "prep launch");
@@ -323,7 +336,7 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
                 reinterpret_cast<const SeqEntry*>(ws + ml.seq_off),
                 reinterpret_cast<const int32_t*>(ws + ml.order_off),
                 reinterpret_cast<const CkptEntry*>(ws + ml.ckpt_off), num_seqs * H, 0, inter, blk,
-                static_cast<uint8_t*>(pool->base), pool->page_bytes};
+                static_cast<uint8_t*>(pool->base), pool->page_bytes, inl ? 1 : 0, 0, iseq, ick};
     Launch L("kda_prefill_scan", st);
     hipError_t e = launch_scan(D, bf, sa, st);
     if (e != hipSuccess) return hip_fail(e, "scan launch");

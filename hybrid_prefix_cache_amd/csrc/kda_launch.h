@@ -8,16 +8,32 @@
 
 namespace kda {
 
+// Small calls carry their sequence and checkpoint tables inside the kernel
+// arguments (read from the kernel-argument segment with scalar loads), which
+// saves the table-fill launch; larger ones read them from the workspace.
+constexpr int kInlineSeqs = 16;
+constexpr int kInlineCkpts = 64;
+struct InlineSeqs {
+  SeqEntry e[kInlineSeqs];
+  int32_t order[kInlineSeqs];  // sequences by descending length
+};
+struct InlineCkpts {
+  CkptEntry e[kInlineCkpts];
+};
+
 struct PrepArgs {
   const void* q;
   const void* k;
   const void* g;
   const void* beta;
-  const SeqEntry* seqs;
+  const SeqEntry* seqs;  // workspace table (when !inline_meta)
   int32_t num_seqs;
   int32_t H;
   uint8_t* inter;
   int64_t blk_bytes;
+  int32_t inline_meta;
+  int32_t pad;
+  InlineSeqs iseq;
 };
 
 struct ScanArgs {
@@ -34,7 +50,12 @@ struct ScanArgs {
   int64_t blk_bytes;
   uint8_t* pool;
   int64_t page_bytes;
+  int32_t inline_meta;
+  int32_t pad2;
+  InlineSeqs iseq;
+  InlineCkpts ick;
 };
+static_assert(sizeof(ScanArgs) <= 4096 && sizeof(PrepArgs) <= 4096, "kernel argument budget");
 
 constexpr int kMaxVerifyTokens = 64;  // tokens per request in one decode launch
 
@@ -120,6 +141,22 @@ __device__ __forceinline__ SeqEntry load_seq(ConstSeqPtr p, int i) {
   e.ckpt_begin = p[i].ckpt_begin;
   e.ckpt_end = p[i].ckpt_end;
   return e;
+}
+// Sequence i of a prefill call, from the kernel arguments or from the
+// workspace table.
+template <typename Args>
+__device__ __forceinline__ SeqEntry seq_at(const Args& a, int i) {
+  return a.inline_meta ? a.iseq.e[i] : load_seq((ConstSeqPtr)(a.seqs), i);
+}
+// Largest s with seq_at(a, s).chunk_begin <= chunk.
+template <typename Args>
+__device__ __forceinline__ int find_seq_in(const Args& a, int chunk) {
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq_at(a, mid).chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 // One kda_short_conv call: 16-token blocks of the 64-token chunks of the

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // chunks in reverse dispatch order (see prep2_kernel)
   const int chunk = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, H = a.H;
-  const SeqEntry se = a.seqs[find_seq(a.seqs, a.num_seqs, chunk)];
+  const SeqEntry se = seq_at(a, find_seq_in(a, chunk));
   const int lc = chunk - se.chunk_begin;
   const int64_t row0 = se.row_begin + 64LL * lc;
   const int len = min(64, se.len - 64 * lc);
@@ -415,8 +415,7 @@ __device__ __forceinline__ void prep2_load(const PrepArgs& a, int pair, int t, P
   const int H = a.H;
   const int chunk = __builtin_amdgcn_readfirstlane(pair / H);
   const int h = __builtin_amdgcn_readfirstlane(pair - chunk * H);
-  const ConstSeqPtr cs = (ConstSeqPtr)(a.seqs);
-  const SeqEntry se = load_seq(cs, find_seq(cs, a.num_seqs, chunk));
+  const SeqEntry se = seq_at(a, find_seq_in(a, chunk));
   const int lc = chunk - se.chunk_begin;
   const int64_t row0 = se.row_begin + 64LL * lc;
   const int len = min(64, se.len - 64 * lc);
@@ -927,7 +926,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   const int p = blk * 8 + xcd;
   if (p >= a.npairs) return;
   const int H = a.H, h = p % H;
-  const SeqEntry se = a.seqs[a.order[p / H]];
+  const SeqEntry se = a.inline_meta ? a.iseq.e[a.iseq.order[p / H]] : load_seq((ConstSeqPtr)(a.seqs), a.order[p / H]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches per role
   ScanCtx c;
@@ -997,7 +996,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   // read through the constant address space: a vector load here would wait
   // for every operand load in flight
   const ConstCkptPtr ck = (ConstCkptPtr)(a.ckpts);
-  int64_t next_pos = nck < se.ckpt_end ? ck[nck].pos : -1;
+  auto ck_pos = [&](int i) -> int64_t { return a.inline_meta ? a.ick.e[i].pos : ck[i].pos; };
+  auto ck_page = [&](int i) -> int { return a.inline_meta ? a.ick.e[i].page : ck[i].page; };
+  int64_t next_pos = nck < se.ckpt_end ? ck_pos(nck) : -1;
 
   auto step = [&](CO& cur, CO& pre, int n) {
     const int nf = min(n + PF, nchunks - 1);  // chunk whose operands are prefetched
@@ -1108,9 +1109,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       }
     }
     if (se.start_pos + 64LL * n + len == next_pos) {
-      s_store(ck[nck].page);
+      s_store(ck_page(nck));
       ++nck;
-      next_pos = nck < se.ckpt_end ? ck[nck].pos : -1;
+      next_pos = nck < se.ckpt_end ? ck_pos(nck) : -1;
     }
     s_to_lds();
   };

@@ -230,6 +230,32 @@ def test_long_1m():
         assert np.all(np.isfinite(pb.states(m)))
 
 
+def test_metadata_paths_bitwise():
+    """Calls with at most 16 sequences and 64 checkpoints carry their tables in
+    the kernel arguments, larger ones in the workspace: 20 sequences with a
+    checkpoint each in one call (workspace tables) must equal, bit for bit, the
+    same sequences in two calls of 10 (inline tables)."""
+    H, D, dtype = 2, 128, "bf16"
+    lens = [600 + 64 * (i % 7) + (i * 37) % 50 for i in range(20)]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    d = G.kda_tokens(4321, H, D, 0, int(cu[-1]), dtype)
+    di = inputs_to_dev(d, dtype)
+    ck = [512] * 20
+    pb = PoolBuf(80, H, D)
+    o_all = prefill(pb, di, cu, dtype, ckpt_cu=np.arange(21), ckpt_pos=ck, ckpt_page=list(range(20)),
+                    state_out_page=list(range(20, 40)))
+    outs = []
+    for half in range(2):
+        a, b = 10 * half, 10 * half + 10
+        sub = {k: v[int(cu[a]):int(cu[b])] for k, v in di.items()}
+        outs.append(prefill(pb, sub, cu[a:b + 1] - cu[a], dtype, ckpt_cu=np.arange(11), ckpt_pos=ck[a:b],
+                            ckpt_page=list(range(40 + a, 40 + b)), state_out_page=list(range(60 + a, 60 + b))))
+    assert torch.equal(o_all, torch.cat(outs, dim=0))
+    for s in range(20):
+        assert np.array_equal(pb.states(s), pb.states(40 + s))        # checkpoints
+        assert np.array_equal(pb.states(20 + s), pb.states(60 + s))   # final states
+
+
 def test_graph_replay_bitwise():
     """The prefill call captured once in a HIP graph (metadata travels in kernel
     arguments, so nothing is re-validated at replay) and replayed three times,
