@@ -45,8 +45,20 @@ template <int D> struct DecodeShape {
 __device__ __forceinline__ float in_f(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float in_f(float x) { return x; }
 
-template <int D, typename In>
-__global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArgs a) {
+// Inputs of one token that a thread reads (its rows' g, k, q; the v column
+// quad of the threads that form u; beta), raw.
+template <int D, typename In> struct TokIn {
+  In g[DecodeShape<D>::VPT], k[DecodeShape<D>::VPT], q[DecodeShape<D>::VPT];
+  In v[4];
+  In beta;
+};
+
+// MULTI (K > 1, speculative verification): the inputs of token t+1 are loaded
+// while token t is applied.  That needs more than the 64 registers that let
+// two 1024-thread workgroups share a CU, so a single-token step (MULTI false)
+// keeps its loads where they are used and the 64-register shape.
+template <int D, typename In, bool MULTI>
+__global__ __launch_bounds__(DecodeShape<D>::NT, MULTI ? 4 : 8) void decode_kernel(DecodeArgs a) {
   using SH = DecodeShape<D>;
   constexpr int VPT = SH::VPT, NQ = SH::NQ, NW = SH::NW, RS = SH::RS;
   __shared__ f32x4 red[2][NW][NQ];
@@ -87,6 +99,23 @@ __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArg
     }
     return x;
   };
+  auto load_tok = [&](int t, TokIn<D, In>& x) {
+    const int64_t row = (int64_t)(r * K + t) * a.H + h;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t c = row * D + rg + i * RS;
+      x.g[i] = reinterpret_cast<const In*>(a.g)[c];
+      x.k[i] = reinterpret_cast<const In*>(a.k)[c];
+      x.q[i] = reinterpret_cast<const In*>(a.q)[c];
+    }
+    if (tid < NQ) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x.v[j] = reinterpret_cast<const In*>(a.v)[row * D + 4 * tid + j];
+    }
+    x.beta = reinterpret_cast<const In*>(a.beta)[row];
+  };
+  TokIn<D, In> cur, nxt;  // MULTI: this token's inputs and the next token's
+  if constexpr (MULTI) load_tok(0, cur);
   for (int t = 0; t < K; ++t) {
     const int par = t & 1;
     const int64_t row = (int64_t)(r * K + t) * a.H + h;  // (token, head) input row
@@ -94,14 +123,24 @@ __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArg
     const In* gk = reinterpret_cast<const In*>(a.k) + row * D;
     const In* gv = reinterpret_cast<const In*>(a.v) + row * D;
     const In* gg = reinterpret_cast<const In*>(a.g) + row * D;
+    if constexpr (MULTI) {
+      if (t + 1 < K) load_tok(t + 1, nxt);
+    }
     float kr[VPT], qr[VPT];
     f32x4 p = zero4();
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {  // S' = diag(alpha) S ; partial S'^T k over this thread's rows
       const int c = rg + i * RS;
-      const float ac = __expf(in_f(gg[c]));
-      kr[i] = in_f(gk[c]);
-      qr[i] = in_f(gq[c]);
+      float ac;
+      if constexpr (MULTI) {
+        ac = __expf(in_f(cur.g[i]));
+        kr[i] = in_f(cur.k[i]);
+        qr[i] = in_f(cur.q[i]);
+      } else {
+        ac = __expf(in_f(gg[c]));
+        kr[i] = in_f(gk[c]);
+        qr[i] = in_f(gq[c]);
+      }
       s[i] *= ac;
       p += s[i] * kr[i];
     }
@@ -113,12 +152,20 @@ __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArg
 #pragma unroll
       for (int w = 1; w < NW; ++w) acc += red[par][w][tid];
       const int c = 4 * tid;
-      sh_u[par][tid] = f32x4{in_f(gv[c]) - acc.x, in_f(gv[c + 1]) - acc.y, in_f(gv[c + 2]) - acc.z,
-                             in_f(gv[c + 3]) - acc.w};  // u = v - S'^T k
+      if constexpr (MULTI) {
+        const TokIn<D, In>& x = cur;
+        sh_u[par][tid] = f32x4{in_f(x.v[0]) - acc.x, in_f(x.v[1]) - acc.y, in_f(x.v[2]) - acc.z,
+                               in_f(x.v[3]) - acc.w};  // u = v - S'^T k
+      } else {
+        sh_u[par][tid] = f32x4{in_f(gv[c]) - acc.x, in_f(gv[c + 1]) - acc.y, in_f(gv[c + 2]) - acc.z,
+                               in_f(gv[c + 3]) - acc.w};  // u = v - S'^T k
+      }
     }
     __syncthreads();
     const f32x4 u = sh_u[par][cq];
-    const float beta = in_f(reinterpret_cast<const In*>(a.beta)[row]);
+    float beta;
+    if constexpr (MULTI) beta = in_f(cur.beta);
+    else beta = in_f(reinterpret_cast<const In*>(a.beta)[row]);
     float* dst = reinterpret_cast<float*>(a.pool + a.page_out[r * K + t] * a.page_bytes) + hoff;
     f32x4 pq = zero4();
 #pragma unroll
@@ -140,19 +187,24 @@ __global__ __launch_bounds__(DecodeShape<D>::NT, 8) void decode_kernel(DecodeArg
       else
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + oi) = acc;
     }
+    if constexpr (MULTI) cur = nxt;
   }
 }
 
+template <int D, typename In>
+static void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.n * (unsigned)a.H), block(DecodeShape<D>::NT);
+  if (a.K > 1) hipLaunchKernelGGL((decode_kernel<D, In, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((decode_kernel<D, In, false>), grid, block, 0, st, a);
+}
+
 hipError_t launch_decode(int D, bool bf16, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.n * (unsigned)a.H);
   if (D == 128) {
-    const dim3 block(DecodeShape<128>::NT);
-    if (bf16) hipLaunchKernelGGL((decode_kernel<128, uint16_t>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<128, float>), grid, block, 0, st, a);
+    if (bf16) launch_decode_t<128, uint16_t>(a, st);
+    else launch_decode_t<128, float>(a, st);
   } else {
-    const dim3 block(DecodeShape<64>::NT);
-    if (bf16) hipLaunchKernelGGL((decode_kernel<64, uint16_t>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((decode_kernel<64, float>), grid, block, 0, st, a);
+    if (bf16) launch_decode_t<64, uint16_t>(a, st);
+    else launch_decode_t<64, float>(a, st);
   }
   return hipGetLastError();
 }
