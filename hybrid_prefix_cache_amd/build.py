@@ -20,6 +20,9 @@ ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          # no packed fp32 instructions (v_pk_*_f32) in device code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core results in ordinary VGPRs: otherwise the prep kernels
+         # copy ~150 accumulator values per pair out of AGPRs one at a time
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
 
