@@ -14,8 +14,10 @@
 //   Kt = K*e, Kh = K/e, Qt = Q*e, Kend = K*(e_C/e)
 //   A  = strictLower(Kt Kh^T) ; Aq = lowerIncl(Qt Kh^T)
 //   T  = (I + diag(beta) A)^-1 diag(beta)
-//   Keff = T Kt ; Qeff = Qt - Aq Keff ; P = Aq T
-//   W = T V - Keff S0 ; O = Qeff S0 + P V ; S_C = diag(e_C) S0 + Kend^T W
+//   Keff = T Kt
+//   W = T V - Keff S0 ; O = Qt S0 + Aq W ; S_C = diag(e_C) S0 + Kend^T W
+// (O = (Qt - Aq Keff) S0 + Aq T V: the query side of each token sees the
+// state entering the chunk plus the chunk's own corrected values W.)
 // Everything left of "W =" is independent of the state and is computed by
 // `prep_kernel` for all (chunk, head) pairs at once; `scan_kernel` walks the
 // chunks of one (sequence, head, 16-column slab of d_v) in order, keeping its
@@ -77,13 +79,13 @@ __device__ __forceinline__ void store8(float* p, const float* x) {
 // (zero-length sequences share their successor's chunk_begin).
 // Offsets (in Op elements) of the pieces of one (chunk, head) block.  Every
 // piece is stored fragment-major (see frag_off) as the scan's MFMA operand:
-// Keff, Qeff, T, P by token rows, KendT by channel rows.
+// Keff, Qt, T, Aq by token rows, KendT by channel rows.
 template <int D> struct InterOff {
   static constexpr int kKeff = 0;
-  static constexpr int kQeff = 64 * D;
+  static constexpr int kQt = 64 * D;
   static constexpr int kKendT = 128 * D;
   static constexpr int kT = 192 * D;
-  static constexpr int kP = 192 * D + 64 * 64;
+  static constexpr int kAq = 192 * D + 64 * 64;
   static constexpr int kGammaElems = 192 * D + 2 * 64 * 64;  // fp32 gamma starts here
 };
 
@@ -91,52 +93,37 @@ template <int D> struct InterOff {
 // prep: state-independent part of every (chunk, head)
 // ---------------------------------------------------------------------------
 
-// LDS plan.  bf16: transposed copies (KtT, TbT, KeffT) keep every MFMA operand
-// K-contiguous.  fp32: operands are read element-wise, so no transposed copies;
-// T is formed in place of the inverse, Keff reuses Kh's space.
-template <int D, typename Op> struct PrepLayout {
-  static constexpr bool kBf = sizeof(Op) == 2;
-  static constexpr int PAD = kBf ? 8 : (D == 128 ? 0 : 4);
-  static constexpr int LDK = D + PAD;  // [64][D] tiles
-  static constexpr int LDC = 64 + (kBf ? 8 : 4);  // [*][64] tiles
-  static constexpr int LDF = 65;       // fp32 solve tiles [64][65]
-  static constexpr int kTile = 64 * LDK * (int)sizeof(Op);
+// LDS plan of the fp32-input prep: operands are read element-wise, so no
+// transposed copies; T is formed in place of the inverse.
+template <int D> struct PrepLayout {
+  static constexpr int LDK = D + (D == 128 ? 0 : 4);  // [64][D] tiles
+  static constexpr int LDF = 65;                      // fp32 solve tiles [64][65]
+  static constexpr int kTile = 64 * LDK * 4;
   static constexpr int kKt = 0;
   static constexpr int kKh = kKt + kTile;
   static constexpr int kQt = kKh + kTile;
-  static constexpr int kKtT = kQt + kTile;
-  static constexpr int kKtTBytes = kBf ? D * LDC * 2 : 0;
-  static constexpr int kR0 = kKtT + kKtTBytes;
+  static constexpr int kR0 = kQt + kTile;
   static constexpr int kR0Bytes = (64 * D * 4 > 2 * 64 * LDF * 4) ? 64 * D * 4 : 2 * 64 * LDF * 4;
-  static constexpr int kKeffT = kR0 + kR0Bytes;  // bf16 only: [D][LDC]
-  static constexpr int kKeffTBytes = kBf ? D * LDC * 2 : 0;
-  static constexpr int kTb = kKeffT + kKeffTBytes;  // bf16 only: [64][LDC]
-  static constexpr int kTbT = kTb + (kBf ? 64 * LDC * 2 : 0);
-  static constexpr int kAq = kTbT + (kBf ? 64 * LDC * 2 : 0);  // [64][LDC]
-  static constexpr int kY = kAq + 64 * LDC * (int)sizeof(Op);   // fp32 [3][16][17]
-  static constexpr int kBeta = kY + 3 * 16 * 17 * 4;            // fp32 [64]
+  static constexpr int kY = kR0 + kR0Bytes;     // fp32 [3][16][17]
+  static constexpr int kBeta = kY + 3 * 16 * 17 * 4;  // fp32 [64]
   static constexpr int kBytes = kBeta + 64 * 4;
   static_assert(kBytes <= 160 * 1024, "prep LDS budget");
 };
 
 template <int D, typename Op>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-  using LY = PrepLayout<D, Op>;
+  static_assert(sizeof(Op) == 4, "bf16 inputs are prepared by prep2_kernel");
+  using LY = PrepLayout<D>;
   using OT = OpT<Op>;
-  constexpr int LDK = LY::LDK, LDC = LY::LDC, LDF = LY::LDF;
+  constexpr int LDK = LY::LDK, LDF = LY::LDF;
   constexpr int KK = OT::kK;
   extern __shared__ __align__(16) uint8_t smem[];
   Op* Kt = reinterpret_cast<Op*>(smem + LY::kKt);
   Op* Kh = reinterpret_cast<Op*>(smem + LY::kKh);
   Op* Qt = reinterpret_cast<Op*>(smem + LY::kQt);
-  Op* KtT = reinterpret_cast<Op*>(smem + LY::kKtT);
   float* Gm = reinterpret_cast<float*>(smem + LY::kR0);  // [64][D] prefix sums
   float* Lm = Gm;                                         // [64][LDF] diag(beta) A
   float* Ti = Gm + 64 * LDF;                              // [64][LDF] inverse, then T (fp32)
-  Op* KeffT = reinterpret_cast<Op*>(smem + LY::kKeffT);
-  Op* Tb = reinterpret_cast<Op*>(smem + LY::kTb);
-  Op* TbT = reinterpret_cast<Op*>(smem + LY::kTbT);
-  Op* Aq = reinterpret_cast<Op*>(smem + LY::kAq);
   float* Y = reinterpret_cast<float*>(smem + LY::kY);
   float* beta_s = reinterpret_cast<float*>(smem + LY::kBeta);
 
@@ -200,7 +187,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
       kh[j] = kx[j] * ei;
       qt[j] = qx[j] * e;
       out[IO::kKendT + frag_off<KK>(c0 + j, r, 64)] = OT::from_f(kx[j] * eci);
-      if constexpr (LY::kBf) KtT[(c0 + j) * LDC + r] = OT::from_f(kt[j]);
+      out[IO::kQt + frag_off<KK>(r, c0 + j, D)] = OT::from_f(qt[j]);
     }
     store8(Kt + r * LDK + c0, kt);
     store8(Kh + r * LDK + c0, kh);
@@ -229,7 +216,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
           if (gram == 0)
             Lm[i * LDF + j] = (j < i) ? beta_s[i] * acc[r] : 0.f;
           else
-            Aq[i * LDC + j] = OT::from_f((j <= i) ? acc[r] : 0.f);
+            out[IO::kAq + frag_off<KK>(i, j, 64)] = OT::from_f((j <= i) ? acc[r] : 0.f);
         }
       }
     }
@@ -276,14 +263,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   for (int it = tid; it < 64 * 64; it += 256) {
     const int i = it >> 6, j = it & 63;
     const float t = (j <= i) ? Ti[i * LDF + j] * beta_s[j] : 0.f;
-    const Op tb = OT::from_f(t);
-    if constexpr (LY::kBf) {
-      Tb[i * LDC + j] = tb;
-      TbT[j * LDC + i] = tb;
-    } else {
-      Ti[i * LDF + j] = t;
-    }
-    out[IO::kT + frag_off<KK>(i, j, 64)] = tb;
+    Ti[i * LDF + j] = t;
+    out[IO::kT + frag_off<KK>(i, j, 64)] = OT::from_f(t);
   }
   __syncthreads();
 
@@ -293,56 +274,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     const int ke = min(64, ((16 * (mt + 1) + KK - 1) / KK) * KK);  // T is lower triangular
     for (int nt = 0; nt < D / 16; ++nt) {
       f32x4 acc = zero4();
-      if constexpr (LY::kBf)
-        tile_mma<Op>(acc, Tb, LDC, 16 * mt, KtT, LDC, 16 * nt, 0, ke, lane);
-      else
-        tile_mma_kn(acc, Ti, LDF, 16 * mt, reinterpret_cast<const float*>(Kt), LDK, 16 * nt, 0, ke,
-                    lane);
+      tile_mma_kn(acc, Ti, LDF, 16 * mt, reinterpret_cast<const float*>(Kt), LDK, 16 * nt, 0, ke, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-        const Op v = OT::from_f(acc[r]);
-        out[IO::kKeff + frag_off<KK>(i, j, D)] = v;
-        if constexpr (LY::kBf)
-          KeffT[j * LDC + i] = v;
-        else
-          Kh[i * LDK + j] = v;  // Keff [64][D] reuses Kh's space
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 6: Qeff = Qt - Aq Keff ; P = Aq T -------------------------------
-  {
-    const int mt = wave;
-    const int ke = min(64, ((16 * (mt + 1) + KK - 1) / KK) * KK);  // Aq is lower triangular
-    for (int nt = 0; nt < D / 16; ++nt) {
-      f32x4 acc = zero4();
-      if constexpr (LY::kBf)
-        tile_mma<Op>(acc, Aq, LDC, 16 * mt, KeffT, LDC, 16 * nt, 0, ke, lane);
-      else
-        tile_mma_kn(acc, reinterpret_cast<const float*>(Aq), LDC, 16 * mt,
-                    reinterpret_cast<const float*>(Kh), LDK, 16 * nt, 0, ke, lane);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-        out[IO::kQeff + frag_off<KK>(i, j, D)] = OT::from_f(OT::to_f(Qt[i * LDK + j]) - acc[r]);
-      }
-    }
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 acc = zero4();
-      if (nt <= mt) {
-        const int kb = ((16 * nt) / KK) * KK;
-        if constexpr (LY::kBf)
-          tile_mma<Op>(acc, Aq, LDC, 16 * mt, TbT, LDC, 16 * nt, kb, ke, lane);
-        else
-          tile_mma_kn(acc, reinterpret_cast<const float*>(Aq), LDC, 16 * mt, Ti, LDF, 16 * nt, kb,
-                      ke, lane);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-        out[IO::kP + frag_off<KK>(i, j, 64)] = OT::from_f(acc[r]);
+        out[IO::kKeff + frag_off<KK>(i, j, D)] = OT::from_f(acc[r]);
       }
     }
   }
@@ -353,10 +289,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 // ---------------------------------------------------------------------------
 // The workgroup (4 waves) owns an LDS region of at most 80 KB whose parts are
 // reused phase by phase:
-//   RA : Kt | Kh (decayed keys)  ->  L | Tinv (fp32 solve)  ->  T | T^T (bf16)
+//   RA : Kt | Kh (decayed keys)  ->  L | Tinv (fp32 solve)  ->  T (bf16)
 //   RQ : Qt (decayed queries)
-//   RT : prefix partials  ->  Kt^T (keys, token-contiguous)  ->  Keff^T
-//   RAQ: Aq (masked Qt Kh^T)
+//   RT : prefix partials  ->  Kt^T (keys, token-contiguous)
 // so two workgroups share a CU and their phases interleave on the SIMDs (two
 // independent workgroups beat one workgroup holding both pairs in lockstep).
 // Element-wise work maps thread -> (channel pair, run of tokens), giving
@@ -375,11 +310,10 @@ template <int D> struct Prep2Layout {
   static constexpr int kRQ = kRA + kRABytes;
   static constexpr int kRT = kRQ + kTileK;
   static constexpr int kRTBytes = (D * LDC * 2 > TPARTS * D * 4) ? D * LDC * 2 : TPARTS * D * 4;
-  static constexpr int kRAQ = kRT + kRTBytes;
-  static constexpr int kBeta = kRAQ + 64 * LDC * 2;  // fp32 beta[64]
+  static constexpr int kBeta = kRT + kRTBytes;  // fp32 beta[64]
   static constexpr int kBytes = kBeta + 64 * 4;
   static_assert(kBytes <= 80 * 1024, "two workgroups must fit in one CU's LDS");
-  static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kRAQ % 16 == 0 && kBytes % 16 == 0, "align");
+  static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kBytes % 16 == 0, "align");
 };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
@@ -466,13 +400,10 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
   uint16_t* Kh = Kt + 64 * LDK;
   float* Lm = reinterpret_cast<float*>(base + LY::kRA);
   float* Ti = Lm + 64 * LDF;
-  uint16_t* Tb = reinterpret_cast<uint16_t*>(base + LY::kRA);
-  uint16_t* TbT = Tb + 64 * LDC;
+  uint16_t* Tb = reinterpret_cast<uint16_t*>(base + LY::kRA);  // inside L's region
   uint16_t* Qt = reinterpret_cast<uint16_t*>(base + LY::kRQ);
   float* partial = reinterpret_cast<float*>(base + LY::kRT);
   uint16_t* KtT = reinterpret_cast<uint16_t*>(base + LY::kRT);
-  uint16_t* KeffT = KtT;
-  uint16_t* Aq = reinterpret_cast<uint16_t*>(base + LY::kRAQ);
   float* beta_s = reinterpret_cast<float*>(base + LY::kBeta);
 
   // Pairs are taken in reverse order: the scan reads chunks first to last, so
@@ -583,9 +514,11 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
 
   // ---- D: Gram matrices, formed transposed (M = key token j, N = token i) ---
   // so that a lane holds 4 consecutive columns j of one row i.  Waves 0,1:
-  // A = Kt Kh^T -> L = diag(beta) strictLower(A) (fp32); waves 2,3:
-  // Aq = lowerIncl(Qt Kh^T) (bf16).  Each wave takes row blocks {0,3} or
-  // {1,2} (5 lower tiles, 3 upper tiles written as zeros for Aq).
+  // A = Kt Kh^T -> L = diag(beta) strictLower(A) (fp32, LDS); waves 2,3:
+  // Aq = lowerIncl(Qt Kh^T) (bf16, to the workspace, as are their Qt
+  // fragments).  Each wave takes row blocks {0,3} or {1,2} (5 lower tiles;
+  // the upper tiles of Aq inside fragments the scan reads are written as
+  // zeros).
   {
     const int gram = wv >> 1;
     const uint16_t* Bop = gram == 0 ? Kt : Qt;
@@ -597,6 +530,11 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
       Frag<uint16_t> bf[NKD];
 #pragma unroll
       for (int k = 0; k < NKD; ++k) bf[k] = frag<uint16_t>(Bop, LDK, 16 * nt, 32 * k, lane);
+      if (gram == 1) {  // Qt rows 16nt.. are one fragment row of the workspace copy
+#pragma unroll
+        for (int k = 0; k < NKD; ++k)
+          *reinterpret_cast<u16x8*>(at32(out, IO::kQt + (uint32_t)((nt * NKD + k) * 64 + lane) * 8u)) = bf[k].v;
+      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {  // column block of j
         acc[pass][mt] = zero4();
@@ -627,11 +565,13 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
       } else {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
+          if (nt < 2 && mt >= 2) continue;  // a zero fragment the scan never reads
           const int j0 = 16 * mt + jq;
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = (j0 + r <= i) ? acc[pass][mt][r] : 0.f;
-          *reinterpret_cast<u16x4*>(Aq + i * LDC + j0) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<u16x4*>(at32(out, IO::kAq + frag_off<32>(i, j0, 64))) =
+              pack_bf16x4(v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -690,14 +630,12 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
   }
   __syncthreads();
   {
-    // T[i][j] = Tinv[i][j] beta_j (j <= i), as bf16, in both orientations:
-    //   row view:    thread -> row i = t / 4, columns 16 (t % 4) .. + 15
-    //   column view: thread -> column j = t / 4, rows 16 (t % 4) .. + 15
-    // Each thread reads its 16 + 16 values before the barrier (T overwrites
-    // Tinv), then writes two 32-byte runs per view; the row view also goes to
-    // global memory (fragment-major, 16-byte runs of 8 columns).
+    // T[i][j] = Tinv[i][j] beta_j (j <= i), as bf16: thread -> row i = t / 4,
+    // columns 16 (t % 4) .. + 15, written as two 32-byte runs to LDS (inside
+    // L's region, which no longer holds anything live) and to the workspace
+    // (fragment-major, 16-byte runs of 8 columns).
     const int rv = t >> 2, g16 = 16 * (t & 3);
-    uint32_t rowp[8], colp[8];
+    uint32_t rowp[8];
     {
       const float* src = Ti + rv * LDF + g16;
 #pragma unroll
@@ -710,34 +648,22 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
         rowp[m / 2] = pack_bf16x2(y[0], y[1]);
         rowp[m / 2 + 1] = pack_bf16x2(y[2], y[3]);
       }
-      const float bj = beta_s[rv];
-#pragma unroll
-      for (int m = 0; m < 16; m += 2) {
-        const int i = g16 + m;
-        const float y0 = (rv <= i) ? Ti[i * LDF + rv] * bj : 0.f;
-        const float y1 = (rv <= i + 1) ? Ti[(i + 1) * LDF + rv] * bj : 0.f;
-        colp[m / 2] = pack_bf16x2(y0, y1);
-      }
     }
-    __syncthreads();  // Tinv is overwritten by T / T^T below
+    static_assert(64 * LDC * 2 <= 64 * LDF * 4, "T fits inside L's region, clear of Tinv");
     uint16_t* tr = Tb + rv * LDC + g16;
-    uint16_t* tc = TbT + rv * LDC + g16;
     const u32x4_t r0v = {rowp[0], rowp[1], rowp[2], rowp[3]}, r1v = {rowp[4], rowp[5], rowp[6], rowp[7]};
     *reinterpret_cast<u32x4_t*>(tr) = r0v;
     *reinterpret_cast<u32x4_t*>(tr + 8) = r1v;
-    *reinterpret_cast<u32x4_t*>(tc) = u32x4_t{colp[0], colp[1], colp[2], colp[3]};
-    *reinterpret_cast<u32x4_t*>(tc + 8) = u32x4_t{colp[4], colp[5], colp[6], colp[7]};
     *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16, 64))) = r0v;
     *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16 + 8, 64))) = r1v;
   }
   __syncthreads();
 
-  // ---- F: Keff = T Kt.  Formed twice: transposed (M = channels) for the
-  // global copy, whose fragments hold 8 consecutive channels of a token, and
-  // direct (M = tokens) for the LDS copy Keff^T, which needs runs of tokens.
-  // T is lower triangular: tokens of row blocks 0, 1 only need k < 32.
+  // ---- F: Keff = T Kt, formed transposed (M = channels) so that each lane
+  // holds 4 consecutive channels of one token, an 8-byte run of the
+  // workspace copy.  T is lower triangular: tokens of row blocks 0, 1 only
+  // need k < 32.
   constexpr int MTW = D / 64;  // channel tiles per wave
-  f32x4 kd[MTW][4];
 #pragma unroll
   for (int u = 0; u < MTW; ++u) {
     const int mt = MTW * wv + u;
@@ -748,50 +674,6 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
       tile_mma<uint16_t>(acc, KtT, LDC, 16 * mt, Tb, LDC, 16 * nt, 0, ke, lane);
       const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
       *reinterpret_cast<u16x4*>(at32(out, IO::kKeff + frag_off<32>(tok, ch, D))) =
-          pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
-      kd[u][nt] = zero4();
-      tile_mma<uint16_t>(kd[u][nt], Tb, LDC, 16 * nt, KtT, LDC, 16 * mt, 0, ke, lane);
-    }
-  }
-  __syncthreads();  // Kt^T is overwritten by Keff^T below
-#pragma unroll
-  for (int u = 0; u < MTW; ++u) {
-    const int mt = MTW * wv + u;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      *reinterpret_cast<u16x4*>(KeffT + (16 * mt + acc_col(lane)) * LDC + 16 * nt + acc_row(lane, 0)) =
-          pack_bf16x4(kd[u][nt][0], kd[u][nt][1], kd[u][nt][2], kd[u][nt][3]);
-  }
-  __syncthreads();
-
-  // ---- G: Qeff^T = Qt^T - Keff^T Aq^T ; P^T = T^T Aq^T ------------------------
-#pragma unroll
-  for (int u = 0; u < MTW; ++u) {
-    const int mt = MTW * wv + u;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 acc = zero4();
-      const int ke = nt < 2 ? 32 : 64;
-      tile_mma<uint16_t>(acc, KeffT, LDC, 16 * mt, Aq, LDC, 16 * nt, 0, ke, lane);
-      const int tok = 16 * nt + acc_col(lane), ch = 16 * mt + acc_row(lane, 0);
-      const u16x4 qv = *reinterpret_cast<const u16x4*>(Qt + tok * LDK + ch);
-      *reinterpret_cast<u16x4*>(at32(out, IO::kQeff + frag_off<32>(tok, ch, D))) =
-          pack_bf16x4(bf16_to_f32(qv[0]) - acc[0], bf16_to_f32(qv[1]) - acc[1],
-                      bf16_to_f32(qv[2]) - acc[2], bf16_to_f32(qv[3]) - acc[3]);
-    }
-  }
-  {
-    // P^T tiles (mt = column block of P, nt = row block): wave wv computes nt = wv
-    const int nt = wv;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = zero4();
-      if (mt <= nt) {
-        const int kb = (16 * mt) / 32 * 32, ke = nt < 2 ? 32 : 64;
-        tile_mma<uint16_t>(acc, TbT, LDC, 16 * mt, Aq, LDC, 16 * nt, kb, ke, lane);
-      }
-      const int tok = 16 * nt + acc_col(lane), col = 16 * mt + acc_row(lane, 0);
-      *reinterpret_cast<u16x4*>(at32(out, IO::kP + frag_off<32>(tok, col, 64))) =
           pack_bf16x4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
@@ -815,16 +697,18 @@ template <int D, int NH> struct ScanGrid {
 // Scan workgroup: 8 waves on one (sequence, head, slab of 16*NH value columns).
 //   waves 0-3 ("W"): rows 16w..16w+15 of W = T V - Keff S          -> LDS
 //   waves 4-7 ("O"): the same rows of O, formed transposed,
-//                    O^T = V^T P^T + S^T Qeff^T, stored as 4-column runs
+//                    O^T = S^T Qt^T (before W is ready) + W^T Aq^T (after),
+//                    stored as 4-column runs
 //   every wave that owns an S tile (rows 16w..16w+15) applies
-//                    S <- diag(gamma_C) S + Kend^T W.
+//                    S <- diag(gamma_C) S + Kend^T W
+//   (the O waves read the same W fragments for both of their products).
 // Each operand fragment feeds NH MFMAs (one per 16-column half), so a wider
 // slab (NH = 2) halves the L2 traffic per column at twice the work per wave.
 // Operands of chunk n+PF are loaded into registers while chunk n computes.
 template <int D, typename Op, int NH> struct ChunkOps {
   static constexpr int KK = OpT<Op>::kK, NKD = D / KK, NKC = 64 / KK;
-  Frag<Op> fa[NKC];  // W waves: T rows; O waves: P rows
-  Frag<Op> fb[NKD];  // W waves: Keff rows; O waves: Qeff rows
+  Frag<Op> fa[NKC];  // W waves: T rows; O waves: Aq rows
+  Frag<Op> fb[NKD];  // W waves: Keff rows; O waves: Qt rows
   Frag<Op> fe[NKC];  // Kend^T rows of the wave's S tile
   f32x4 gam;         // gamma_C of the 4 S rows this lane holds
   // 2*NH V values of this thread, kept in the input encoding until used
@@ -856,8 +740,8 @@ template <int D, typename Op, int NH>
 __device__ __forceinline__ void load_ops_a(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
   using CO = ChunkOps<D, Op, NH>;
   using IO = InterOff<D>;
-  const Op* pa = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kP : IO::kT);
-  // T and P are lower triangular: a row tile's fragments right of its
+  const Op* pa = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kAq : IO::kT);
+  // T and Aq are lower triangular: a row tile's fragments right of its
   // diagonal block are zero and are neither loaded nor multiplied
 #pragma unroll
   for (int i = 0; i < CO::NKC; ++i)
@@ -868,7 +752,7 @@ template <int D, typename Op, int NH>
 __device__ __forceinline__ void load_ops_b(ChunkOps<D, Op, NH>& f, const ScanCtx& c, int n) {
   using CO = ChunkOps<D, Op, NH>;
   using IO = InterOff<D>;
-  const Op* pb = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kQeff : IO::kKeff);
+  const Op* pb = chunk_block<D, Op>(c, n) + (c.is_o ? IO::kQt : IO::kKeff);
 #pragma unroll
   for (int i = 0; i < CO::NKD; ++i) f.fb[i] = frag_fm<Op>(pb, c.wv & 3, i, D, c.lane);
 }
@@ -1027,6 +911,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
     // registers before the first MFMA, and accumulates in independent halves
     // that are summed at the end: the chains are then as short as the
     // matrix-core dependency allows instead of one LDS round trip per MFMA.
+    f32x4 OQ[NH];  // O waves: S^T Qt^T, completed after the barrier
     if (!c.is_o) {
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
@@ -1059,32 +944,53 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
           *reinterpret_cast<f32x4*>(wdst) = Wv;
       }
     } else {
-      const int tok = 16 * rt + acc_col(lane);
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        // O^T[col = 16j + 4*(lane/16) + r][token = 16*rt + lane%16]
-        f32x4 OA = zero4(), OB0 = zero4(), OB1 = zero4();
+        // O^T[col = 16j + 4*(lane/16) + r][token = 16*rt + lane%16], first part
+        f32x4 OB0 = zero4(), OB1 = zero4();
         if constexpr (kBatchLds) {
-          Frag<Op> vf[CO::NKC], sf[CO::NKD];
-#pragma unroll
-          for (int i = 0; i < CO::NKC; ++i)
-            if (i * KK <= 16 * rt + 15) vf[i] = frag<Op>(Vb, LDW, 16 * j, i * KK, lane);
+          Frag<Op> sf[CO::NKD];
 #pragma unroll
           for (int i = 0; i < CO::NKD; ++i) sf[i] = frag<Op>(Sb, LDS_, 16 * j, i * KK, lane);
-#pragma unroll
-          for (int i = 0; i < CO::NKC; ++i)
-            if (i * KK <= 16 * rt + 15) mfma(OA, vf[i], cur.fa[i]);
 #pragma unroll
           for (int i = 0; i < CO::NKD; ++i) mfma(i < CO::NKD / 2 ? OB0 : OB1, sf[i], cur.fb[i]);
         } else {
 #pragma unroll
-          for (int i = 0; i < CO::NKC; ++i)
-            if (i * KK <= 16 * rt + 15) mfma(OA, frag<Op>(Vb, LDW, 16 * j, i * KK, lane), cur.fa[i]);
-#pragma unroll
           for (int i = 0; i < CO::NKD; ++i)
             mfma(i < CO::NKD / 2 ? OB0 : OB1, frag<Op>(Sb, LDS_, 16 * j, i * KK, lane), cur.fb[i]);
         }
-        const f32x4 OT4 = OA + OB0 + OB1;
+        OQ[j] = OB0 + OB1;
+      }
+    }
+    __syncthreads();  // Wb ready; every wave is done reading Sb and Vb
+    load_ops_c<D, Op, NH>(pre, c, nf);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // S <- diag(gamma_C) S + Kend^T W on the waves that own an S tile;
+    // O^T += W^T Aq^T on the O waves, then the O store
+    const int tok = 16 * rt + acc_col(lane);
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      if (!c.owns_s && !c.is_o) continue;
+      // bf16: the W fragments are read once for both products; fp32 (8x as
+      // many fragments) reads them as the products go
+      Frag<Op> wf[kBatchLds ? CO::NKC : 1];
+      auto wfrag = [&](int i) { return kBatchLds ? wf[i] : frag<Op>(Wb, LDW, 16 * j, i * KK, lane); };
+      if constexpr (kBatchLds) {
+#pragma unroll
+        for (int i = 0; i < CO::NKC; ++i) wf[i] = frag<Op>(Wb, LDW, 16 * j, i * KK, lane);
+      }
+      if (c.owns_s) {
+        S[j] *= cur.gam;
+#pragma unroll
+        for (int i = 0; i < CO::NKC; ++i) mfma(S[j], cur.fe[i], wfrag(i));
+      }
+      if (c.is_o) {
+        f32x4 OA = zero4();
+#pragma unroll
+        for (int i = 0; i < CO::NKC; ++i)
+          if (i * KK <= 16 * rt + 15) mfma(OA, wfrag(i), cur.fa[i]);
+        const f32x4 OT4 = OA + OQ[j];
         if (tok < len) {
           const int64_t base =
               ((c.row_begin + 64LL * n + tok) * H + h) * D + c.c0 + 16 * j + acc_row(lane, 0);
@@ -1094,18 +1000,6 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
           else
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + base) = OT4;
         }
-      }
-    }
-    __syncthreads();  // Wb ready; every wave is done reading Sb and Vb
-    load_ops_c<D, Op, NH>(pre, c, nf);
-    __builtin_amdgcn_sched_barrier(0);
-
-    if (c.owns_s) {  // S <- diag(gamma_C) S + Kend^T W
-#pragma unroll
-      for (int j = 0; j < NH; ++j) {
-        S[j] *= cur.gam;
-#pragma unroll
-        for (int i = 0; i < CO::NKC; ++i) mfma(S[j], cur.fe[i], frag<Op>(Wb, LDW, 16 * j, i * KK, lane));
       }
     }
     if (se.start_pos + 64LL * n + len == next_pos) {
@@ -1149,7 +1043,7 @@ hipError_t launch_meta_fill(const MetaFillArgs& a, hipStream_t st) {
 
 template <int D, typename Op>
 static hipError_t launch_prep_t(const PrepArgs& a, int total_chunks, hipStream_t st) {
-  using LY = PrepLayout<D, Op>;
+  using LY = PrepLayout<D>;
   // Opt in to more than 64 KiB of dynamic LDS (best effort; the launch reports
   // any real failure).
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel<D, Op>),

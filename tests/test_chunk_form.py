@@ -9,9 +9,8 @@ inside a chunk of C tokens with entering state S0, let G_r = sum_{i<=r} g_i
     A  = strictLower(Kt Kh^T),   Aq = lowerIncl(Qt Kh^T),
     T  = (I + diag(beta) A)^-1 diag(beta).
 Then  W = T (V - Kt S0),  O = Qt S0 + Aq W,  S_C = diag(e_C) S0 + Kend^T W.
-The GPU keeps the S-independent parts precomputed:
-    Keff = T Kt, Qeff = Qt - Aq Keff, P = Aq T, so that
-    W = T V - Keff S0,  O = Qeff S0 + P V.
+The GPU keeps the S-independent parts precomputed (Keff = T Kt, Qt, Aq, T,
+Kend), so that W = T V - Keff S0 and O = Qt S0 + Aq W.
 A partial final chunk is padded with k = q = v = g = beta = 0 rows, which leave
 the state unchanged.  This is a CPU model of the GPU algorithm; the oracle it
 is compared with is the token loop.
@@ -39,10 +38,8 @@ def chunk_prefill(q, k, v, g, beta, s0, C=64):
         Aq = np.tril(Qt @ Kh.T)
         Tm = np.linalg.solve(np.eye(C) + b[:, None] * A, np.diag(b))
         Keff = Tm @ Kt
-        Qeff = Qt - Aq @ Keff
-        P = Aq @ Tm
         W = Tm @ V - Keff @ S
-        O = Qeff @ S + P @ V
+        O = Qt @ S + Aq @ W
         S = e[-1][:, None] * S + Kend.T @ W
         o[c0:c0 + n] = O[:n]
     return o, S
