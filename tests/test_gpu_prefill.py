@@ -298,3 +298,24 @@ def test_graph_replay_bitwise():
         for p in (1, 2):
             assert np.array_equal(got_pool[p * sw:(p + 1) * sw], ref_pool[p * sw:(p + 1) * sw])
         assert np.all(got_pool[:sw] == poison)  # page 0 is not an output of the call
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_slab_width_bitwise(dtype, monkeypatch):
+    """Every value column of the state is carried on its own (the d_v split), so
+    16- and 32-column slabs (KDA_SCAN_SLAB=1 / 2 overrides the size-based choice)
+    give bit-identical o, checkpoints and final states."""
+    H, D = 4, 128
+    cu = np.array([0, 700, 2000])
+    d = G.kda_tokens(99, H, D, 0, int(cu[-1]), dtype)
+    di = inputs_to_dev(d, dtype)
+    res = []
+    for nh in ("1", "2"):
+        monkeypatch.setenv("KDA_SCAN_SLAB", nh)
+        pb = PoolBuf(4, H, D)
+        o = prefill(pb, di, cu, dtype, ckpt_cu=[0, 1, 2], ckpt_pos=[512, 1024], ckpt_page=[0, 1],
+                    state_out_page=[2, 3])
+        res.append((o.cpu(), pb.snapshot()))
+    assert torch.equal(res[0][0].view(torch.int16) if dtype == "bf16" else res[0][0],
+                       res[1][0].view(torch.int16) if dtype == "bf16" else res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
