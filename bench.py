@@ -128,6 +128,44 @@ def summarize_pmc(fetch_dir, write_dir, command):
     return "\n".join(lines) + "\n"
 
 
+UTIL_COUNTERS = ("MfmaUtil", "VALUBusy", "LdsUtil", "MfmaFlopsBF16", "MfmaFlopsF32")
+
+
+def summarize_util(util_dir, command):
+    """Markdown summary of one rocprofv3 --pmc run of this script with the
+    derived counters UTIL_COUNTERS (matrix-core busy %, vector ALU busy %, LDS
+    busy %, MFMA flops per dispatch), averaged per library kernel."""
+    acc = {}
+    for path in glob.glob(os.path.join(util_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                sym = r["Kernel_Name"]
+                name = next((v for k, v in KERNEL_SYMBOLS.items() if f"kda::{k}" in sym), None)
+                if name and r["Counter_Name"] in UTIL_COUNTERS:
+                    acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+    lines = [
+        "# Matrix-core, vector-ALU and LDS activity per launch (rocprofv3 derived counters)", "",
+        "Workloads as in the kernel-trace summary (bench.py --only-core: prefill 8K x 32 heads x d=128",
+        "bf16, decode 256 x 32, page copy, int8 checkpoints, verify, short conv).  Commands (from /tmp,",
+        "TMPDIR=/tmp, R = repository root):", "",
+        "```", *command, "```", "",
+        "MfmaUtil = matrix-core busy cycles / (GPU busy cycles x SIMDs); VALUBusy and LdsUtil likewise",
+        "for vector-ALU instruction issue and LDS; MFMA flops = the counter's MOPS x 512 (dense).",
+        "The prefill's algorithmic work is 131,072 flop per (token, head), 34.36 GFLOP per 8K x 32-head",
+        "call; what the kernels execute on the matrix cores includes the masked halves of the",
+        "triangular products and the per-slab repetition of the state products.", "",
+        "| kernel | MfmaUtil % | VALUBusy % | LdsUtil % | MFMA bf16 GFLOP | MFMA fp32 GFLOP |",
+        "|---|---|---|---|---|---|",
+    ]
+    for name in sorted(avg):
+        d = avg[name]
+        g = lambda c: d.get(c, float("nan"))
+        lines.append(f"| {name} | {g('MfmaUtil'):.1f} | {g('VALUBusy'):.1f} | {g('LdsUtil'):.1f} | "
+                     f"{g('MfmaFlopsBF16') / 1e9:.2f} | {g('MfmaFlopsF32') / 1e9:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def to_dev(x, dtype):
     import torch
     if dtype == "bf16":
@@ -531,7 +569,15 @@ def main():
                     help="skip the resume and 2^20-token workloads (profiling runs: one prefill shape)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the markdown traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-util", metavar="UTIL_DIR",
+                    help="print the markdown summary of a rocprofv3 --pmc run of UTIL_COUNTERS and exit")
     args = ap.parse_args()
+    if args.summarize_util:
+        cmd = [f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d $R/gpurun_out/pmc_util "
+               f"-o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu --only-core",
+               "python3 $R/bench.py --summarize-util $R/gpurun_out/pmc_util"]
+        sys.stdout.write(summarize_util(args.summarize_util, cmd))
+        return
     if args.summarize_pmc:
         cmd = [f"rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{d} -o run -- "
                f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu --only-core"
