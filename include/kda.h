@@ -161,6 +161,9 @@ size_t kda_prefill_workspace_bytes(const kda_pool* pool, int64_t total_tokens, i
  * Domain: the chunk form factors the decay as exp(+G) and exp(-G) with G the
  * within-chunk prefix sum of g; it needs |G| < 80 in every channel of every
  * chunk (mean log alpha > -1.25 per token).
+ * Tuning: the environment variable KDA_SCAN_SLAB=1 or 2 forces 16- or
+ * 32-column state slabs in the scan (by default 32 when that still gives every
+ * CU a workgroup); results are bit-identical either way.
  */
 kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* k, const void* v,
                                const void* g, const void* beta, kda_dtype in_dtype, void* o,
