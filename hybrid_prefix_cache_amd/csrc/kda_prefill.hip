@@ -25,6 +25,7 @@
 // which is what allows the d_v split.  A partial final chunk is padded with
 // zero rows (k = q = v = g = beta = 0), which leave the state unchanged.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -1059,18 +1060,19 @@ static hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; calls from
+// several host threads may race to fill an entry, all with the same value).
 static int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int D>
