@@ -29,7 +29,9 @@ static_assert(sizeof(CkptEntry) == 16, "CkptEntry layout");
 // Workspace bytes per (chunk, head) block of prefill intermediates, element
 // type Op (bf16 or fp32):
 //   Keff [64][D], Qt [64][D], KendT [D][64], T [64][64], Aq [64][64],
-//   then gammaC [D] fp32; padded to 256 bytes.
+//   then gammaC [D] fp32; padded to 256 bytes.  With bf16 operands the two
+//   16x32 fragments right of the diagonal in row tiles 0 and 1 of T and of
+//   Aq are zero, never written and never read.
 inline constexpr int64_t inter_elems(int D) { return 3LL * 64 * D + 2LL * 64 * 64; }
 inline constexpr int64_t inter_block_bytes(int D, int op_bytes) {
   return ((inter_elems(D) * op_bytes + 4LL * D) + 255) / 256 * 256;

@@ -655,8 +655,12 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
     const u32x4_t r0v = {rowp[0], rowp[1], rowp[2], rowp[3]}, r1v = {rowp[4], rowp[5], rowp[6], rowp[7]};
     *reinterpret_cast<u32x4_t*>(tr) = r0v;
     *reinterpret_cast<u32x4_t*>(tr + 8) = r1v;
-    *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16, 64))) = r0v;
-    *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16 + 8, 64))) = r1v;
+    // rows 0..31 are zero right of column 31: the scan never reads those two
+    // fragments, so they are not written
+    if (rv >= 32 || g16 < 32) {
+      *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16, 64))) = r0v;
+      *reinterpret_cast<u32x4_t*>(at32(out, IO::kT + frag_off<32>(rv, g16 + 8, 64))) = r1v;
+    }
   }
   __syncthreads();
 
