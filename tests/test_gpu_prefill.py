@@ -319,3 +319,31 @@ def test_slab_width_bitwise(dtype, monkeypatch):
     assert torch.equal(res[0][0].view(torch.int16) if dtype == "bf16" else res[0][0],
                        res[1][0].view(torch.int16) if dtype == "bf16" else res[1][0])
     assert np.array_equal(res[0][1], res[1][1])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_unwritten_workspace_never_read(dtype, D):
+    """Workspace bytes that a call does not write (the zero fragments of the
+    triangular intermediates, padding) are never read: a workspace filled with
+    NaN bit patterns (every byte 0xFF) and one filled with zeros give finite,
+    bit-identical o, checkpoints and final states."""
+    H, cu = 4, [0, 700, 2000]
+    d = G.kda_tokens(101, H, D, 0, cu[-1], dtype)
+    di = inputs_to_dev(d, dtype)
+    ind = K.KDA_BF16 if dtype == "bf16" else K.KDA_F32
+    res = []
+    for fill in (0, 255):
+        pb = PoolBuf(4, H, D)
+        ws = torch.full((K.kda_prefill_workspace_bytes(pb.pool, cu[-1], 2, 2, ind),), fill,
+                        dtype=torch.uint8, device="cuda")
+        o = torch.full((cu[-1], H, D), float("nan"), device="cuda",
+                       dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+        K.kda_prefill_chunked(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, cu,
+                              workspace=ws, ckpt_cu=[0, 1, 2], ckpt_pos=[512, 1024],
+                              ckpt_page=[0, 1], state_out_page=[2, 3])
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all()
+        res.append(((o.view(torch.int16) if dtype == "bf16" else o.view(torch.int32)).cpu().numpy(),
+                    pb.snapshot()))
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
