@@ -110,7 +110,7 @@ def summarize_pmc(fetch_dir, write_dir, command):
         "# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
         "Workloads: prefill 8K x 32 heads x d=128 bf16 with 3 checkpoints; decode 256 requests x",
         "32 heads; page copy 256 x 2 MiB; int8 checkpoint write / restore of 256 pages.  Commands",
-        "(from /tmp, TMPDIR=/tmp, R = repository root):", "",
+        "(from /tmp, TMPDIR=/tmp, R = repository root, OUT = the profiler's output directory):", "",
         "```", *command, "```", "",
         f"Calibration against the page copy (512 MiB read + 512 MiB written per launch): "
         f"FETCH_SIZE x {kf:.3f}, WRITE_SIZE x {kw:.3f}.  Source hash = first 16 hex digits of the",
@@ -148,7 +148,7 @@ def summarize_util(util_dir, command):
         "# Matrix-core, vector-ALU and LDS activity per launch (rocprofv3 derived counters)", "",
         "Workloads as in the kernel-trace summary (bench.py --only-core: prefill 8K x 32 heads x d=128",
         "bf16, decode 256 x 32, page copy, int8 checkpoints, verify, short conv).  Commands (from /tmp,",
-        "TMPDIR=/tmp, R = repository root):", "",
+        "TMPDIR=/tmp, R = repository root, OUT = the profiler's output directory):", "",
         "```", *command, "```", "",
         "MfmaUtil = matrix-core busy cycles / (GPU busy cycles x SIMDs); VALUBusy and LdsUtil likewise",
         "for vector-ALU instruction issue and LDS; MFMA flops = the counter's MOPS x 512 (dense).",
@@ -573,16 +573,16 @@ def main():
                     help="print the markdown summary of a rocprofv3 --pmc run of UTIL_COUNTERS and exit")
     args = ap.parse_args()
     if args.summarize_util:
-        cmd = [f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d $R/gpurun_out/pmc_util "
+        cmd = [f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d $OUT/pmc_util "
                f"-o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu --only-core",
-               "python3 $R/bench.py --summarize-util $R/gpurun_out/pmc_util"]
+               "python3 $R/bench.py --summarize-util $OUT/pmc_util"]
         sys.stdout.write(summarize_util(args.summarize_util, cmd))
         return
     if args.summarize_pmc:
-        cmd = [f"rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/{d} -o run -- "
+        cmd = [f"rocprofv3 --pmc {c} --output-format csv -d $OUT/{d} -o run -- "
                f"python3 $R/bench.py --steps 3 --warmup 1 --no-cpu --only-core"
                for c, d in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write"))]
-        cmd.append("python3 $R/bench.py --summarize-pmc $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write")
+        cmd.append("python3 $R/bench.py --summarize-pmc $OUT/pmc_fetch $OUT/pmc_write")
         sys.stdout.write(summarize_pmc(*args.summarize_pmc, cmd))
         return
     if args.gpus != 1:
