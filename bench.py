@@ -586,7 +586,7 @@ def main():
         sys.stdout.write(summarize_pmc(*args.summarize_pmc, cmd))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for "
               f"--gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -7,7 +7,7 @@
 // convolution history and the recurrent checkpoint in the same pass) and 6.5
 // (the convolution state is the window of recent inputs, kept at full
 // precision; a restore needs it as well as the recurrent state).  Width W and
-// the absence of an activation are this build's reading (the pages fix
+// the absence of an activation are this implementation's reading (the pages fix
 // neither):  y[t][c] = sum_{j < W} w[c][j] * x[t - (W-1) + j][c].
 //
 // Work unit: a 16-token block of one 64-token chunk of the sequence table, for

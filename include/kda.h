@@ -274,7 +274,7 @@ kda_status kda_checkpoint_restore_int8(const kda_pool* qpool, const int32_t* src
  * short causal convolution whose state is the window of the most recent inputs;
  * that window is checkpointed with the recurrent state at the same boundary,
  * kept at full precision, and a restore must bring it back too.  The pages fix
- * neither the width nor an activation; this build takes a width W in {2, 3, 4}
+ * neither the width nor an activation; this library takes a width W in {2, 3, 4}
  * and no activation:
  *     y[t][c] = sum_{j < W} w[c][j] * x[t - (W-1) + j][c]
  * with x at positions before a sequence's start taken from its state page
