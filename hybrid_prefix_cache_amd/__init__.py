@@ -163,6 +163,33 @@ class _HostArr:
         return None if self.a is None else self.a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _need_len(name, arr, n):
+    """Raise ValueError unless the host array `arr` (a _HostArr, possibly None)
+    holds exactly n entries: the C side reads n entries through its pointer."""
+    if arr.a is not None and (arr.a.ndim != 1 or len(arr.a) != n):
+        raise ValueError(f"{name} must hold {n} entries (got shape {arr.a.shape})")
+
+
+def _seq_meta_lengths(ns, sp, si, so, ccu, cpos, cpg):
+    """Length checks of the per-sequence and checkpoint host arrays shared by
+    kda_prefill_chunked and kda_short_conv."""
+    for name, arr in (("start_pos", sp), ("state_in_page", si), ("state_out_page", so)):
+        _need_len(name, arr, ns)
+    if ccu.a is None:
+        if cpos.a is not None or cpg.a is not None:
+            raise ValueError("ckpt_pos / ckpt_page given without ckpt_cu")
+        return
+    _need_len("ckpt_cu", ccu, ns + 1)
+    nck = int(ccu.a[-1]) if ns >= 0 else 0
+    if nck > 0 and (cpos.a is None or cpg.a is None):
+        raise ValueError("ckpt_pos and ckpt_page are required when ckpt_cu is given")
+    if nck < 0:
+        raise ValueError("ckpt_cu[-1] must be non-negative")
+    for name, arr in (("ckpt_pos", cpos), ("ckpt_page", cpg)):
+        if arr.a is not None and (arr.a.ndim != 1 or len(arr.a) < nck):
+            raise ValueError(f"{name} must hold ckpt_cu[-1] = {nck} entries (got shape {arr.a.shape})")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -230,6 +257,7 @@ def kda_prefill_chunked(pool, q, k, v, g, beta, o, cu_seqlens, *, start_pos=None
     ccu = _HostArr(ckpt_cu, np.int32)
     cpos = _HostArr(ckpt_pos, np.int64)
     cpg = _HostArr(ckpt_page, np.int32)
+    _seq_meta_lengths(ns, sp, si, so, ccu, cpos, cpg)
     ind = _dtype_code(q) if in_dtype is None else in_dtype
     outd = _dtype_code(o) if out_dtype is None else out_dtype
     if workspace_bytes is None:
@@ -271,11 +299,13 @@ def kda_decode_verify(pool, q, k, v, g, beta, o, tokens, page_in, page_out, *, n
 
 def kda_checkpoint_write(pool, src_active, dst_ckpt, *, stream=None):
     s, d = _HostArr(src_active, np.int32), _HostArr(dst_ckpt, np.int32)
+    _need_len("dst_ckpt", d, len(s.a))
     _check(_lib.kda_checkpoint_write(ctypes.byref(pool), s.ptr, d.ptr, len(s.a), _stream(stream)))
 
 
 def kda_checkpoint_restore(pool, src_ckpt, dst_active, *, stream=None):
     s, d = _HostArr(src_ckpt, np.int32), _HostArr(dst_active, np.int32)
+    _need_len("dst_active", d, len(s.a))
     _check(_lib.kda_checkpoint_restore(ctypes.byref(pool), s.ptr, d.ptr, len(s.a), _stream(stream)))
 
 
@@ -286,12 +316,14 @@ def kda_ckpt_int8_head_bytes(d_k: int, d_v: int) -> int:
 
 def kda_checkpoint_write_int8(pool, src_active, qpool, dst_qckpt, *, stream=None):
     s, d = _HostArr(src_active, np.int32), _HostArr(dst_qckpt, np.int32)
+    _need_len("dst_qckpt", d, len(s.a))
     _check(_lib.kda_checkpoint_write_int8(ctypes.byref(pool), s.ptr, ctypes.byref(qpool), d.ptr,
                                           len(s.a), _stream(stream)))
 
 
 def kda_checkpoint_restore_int8(qpool, src_qckpt, pool, dst_active, *, stream=None):
     s, d = _HostArr(src_qckpt, np.int32), _HostArr(dst_active, np.int32)
+    _need_len("dst_active", d, len(s.a))
     _check(_lib.kda_checkpoint_restore_int8(ctypes.byref(qpool), s.ptr, ctypes.byref(pool), d.ptr,
                                             len(s.a), _stream(stream)))
 
@@ -315,6 +347,7 @@ def kda_short_conv(cpool, x, w, y, cu_seqlens, *, start_pos=None, state_in_page=
     ccu = _HostArr(ckpt_cu, np.int32)
     cpos = _HostArr(ckpt_pos, np.int64)
     cpg = _HostArr(ckpt_page, np.int32)
+    _seq_meta_lengths(ns, sp, si, so, ccu, cpos, cpg)
     outd = _dtype_code(y) if out_dtype is None else out_dtype
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else (

@@ -61,8 +61,23 @@
 
 static inline double ld(const void* p, int dtype, int64_t i) {
   if (dtype == OR_F64) return ((const double*)p)[i];
+#if KDA_ORACLE_MUTANT == 11
+  /* mistake: fp32 inputs truncated to their upper 16 bits */
+  if (dtype == OR_F32) {
+    uint32_t w;
+    memcpy(&w, (const float*)p + i, 4);
+    w &= 0xffff0000u;
+    float t;
+    memcpy(&t, &w, 4);
+    return (double)t;
+  }
+#else
   if (dtype == OR_F32) return (double)((const float*)p)[i];
+#endif
   uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+#if KDA_ORACLE_MUTANT == 9
+  u ^= 0x10000u; /* mistake: lowest mantissa bit of a bf16 input flipped */
+#endif
   float f;
   memcpy(&f, &u, 4);
   return (double)f;
@@ -227,7 +242,11 @@ int kda_oracle_run(int32_t H, int32_t dk, int32_t dv, int32_t num_seqs, const in
     for (int64_t pr = 0; pr < pairs; ++pr) {
       const int32_t s = (int32_t)(pr / n_sel);
       const int32_t hs = (int32_t)(pr % n_sel);
+#if KDA_ORACLE_MUTANT == 10
+      const int32_t h = heads ? heads[0] : hs; /* mistake: first selected head for all */
+#else
       const int32_t h = heads ? heads[hs] : hs;
+#endif
       const int64_t bos = cu_seqlens[s], len = cu_seqlens[s + 1] - bos;
       const int64_t st = start_pos ? start_pos[s] : 0;
       const int32_t m = ckpt_cu ? ckpt_cu[s] : 0;

@@ -261,6 +261,72 @@ def pin_checkpoint_positions(lib_path=None):
     return np.array_equal(r["ckpts"][2], r["s_final"][0]), "ok"
 
 
+# --------------------------------------------------------------------------
+# input decoding and head selection
+# --------------------------------------------------------------------------
+def _bf16_bits(x):
+    """Round-to-nearest-even fp64 -> bf16 bit patterns, done by numpy on the
+    fp32 bit pattern (independent of the oracle's decoding)."""
+    f = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((f + 0x7FFF + ((f >> 16) & 1)) >> 16).astype(np.uint16)
+    return r
+
+
+def _bits_to_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_input_widening(lib_path=None):
+    """The oracle reads bf16 and fp32 inputs exactly: a run on bf16 bit
+    patterns (and on the same values stored as fp32) is bitwise equal to the
+    run on those values already widened to fp64 by numpy.  The inputs use
+    every bf16 mantissa bit (random normals, not short fractions), and the
+    fp32 run also gets values with non-zero low 16 bits."""
+    rng = np.random.default_rng(RNG_SEED + 9)
+    T, H, dk, dv = 13, 3, 6, 5
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    bits = [_bf16_bits(x) for x in (q, k, v, g, beta)]
+    wide = [_bits_to_f64(b) for b in bits]
+    kw = dict(ckpt_cu=np.array([0, 2]), ckpt_pos=np.array([5, 13]))
+    ref = _run(lib_path, *wide, **kw)
+    got_bf = _run(lib_path, *bits, **kw)
+    got_f32 = _run(lib_path, *[w.astype(np.float32) for w in wide], **kw)
+    for name, got in (("bf16", got_bf), ("fp32 (bf16 values)", got_f32)):
+        for key in ("o", "s_final", "ckpts"):
+            if not np.array_equal(got[key], ref[key]):
+                return False, f"{name} inputs decoded differently ({key})"
+    # full fp32 mantissas: fp32 storage vs the same values as fp64
+    f32 = [np.asarray(x, np.float32) for x in (q, k, v, g, beta)]
+    if not any(np.any(x.view(np.uint32) & 0xFFFF) for x in f32):
+        return False, "fixture lacks low fp32 mantissa bits"
+    r32 = _run(lib_path, *f32, **kw)
+    r64 = _run(lib_path, *[x.astype(np.float64) for x in f32], **kw)
+    ok = all(np.array_equal(r32[key], r64[key]) for key in ("o", "s_final", "ckpts"))
+    return ok, "bitwise" if ok else "fp32 inputs decoded differently"
+
+
+def pin_head_subset(lib_path=None):
+    """Running a subset of heads (in any order) gives, bit for bit, the same
+    outputs, final states and checkpoints as the matching slices of the
+    all-heads run, with per-head entering states selected by position."""
+    rng = np.random.default_rng(RNG_SEED + 10)
+    T, H, dk, dv = 17, 4, 5, 3
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    cu = np.array([0, 7, 17])
+    s0 = rng.standard_normal((2, H, dk, dv))
+    kw = dict(ckpt_cu=np.array([0, 1, 2]), ckpt_pos=np.array([4, 12]),
+              start_pos=np.array([0, 2]))
+    full = oracle.run(q, k, v, g, beta, cu, s0=s0, lib_path=lib_path, **kw)
+    sel = np.array([2, 0, 3])
+    sub = oracle.run(q, k, v, g, beta, cu, s0=np.ascontiguousarray(s0[:, sel]), heads=sel,
+                     lib_path=lib_path, **kw)
+    ok = (np.array_equal(sub["o"], full["o"][:, sel]) and
+          np.array_equal(sub["s_final"], full["s_final"][:, sel]) and
+          np.array_equal(sub["ckpts"], full["ckpts"][:, sel]))
+    return ok, "bitwise" if ok else "head subset differs from the all-heads slices"
+
+
 ALL_PINS = [pin_exact_bruteforce, pin_identity, pin_pure_decay, pin_exact_write,
             pin_associative_memory, pin_affine_composition, pin_column_independence,
-            pin_resume, pin_checkpoint_positions]
+            pin_resume, pin_checkpoint_positions, pin_input_widening,
+            pin_head_subset]

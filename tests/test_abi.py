@@ -349,3 +349,26 @@ def test_conv_accepts_checkpoints_past_start_and_empty_batch():
     assert st == K.KDA_OK
     # empty sequences without output pages enqueue nothing
     assert _conv_status(T=0, x=0, y=0) == K.KDA_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(cu_seqlens=[0, 512, 1024], start_pos=[0]),
+    dict(cu_seqlens=[0, 512, 1024], state_in_page=[1]),
+    dict(cu_seqlens=[0, 512, 1024], state_out_page=[1, 2, 3]),
+    dict(ckpt_cu=[0], ckpt_pos=[512], ckpt_page=[3]),
+    dict(ckpt_cu=[0, 2], ckpt_pos=[512], ckpt_page=[3, 4]),
+    dict(ckpt_cu=[0, 2], ckpt_pos=[512, 1024], ckpt_page=[3]),
+    dict(ckpt_cu=[0, 1], ckpt_pos=[512]),
+    dict(ckpt_pos=[512], ckpt_page=[3]),
+])
+def test_prefill_host_array_lengths(kw):
+    """A host array shorter than the count the C side reads through its pointer
+    is refused by the binding before the call (no out-of-bounds host read)."""
+    with pytest.raises(ValueError):
+        _prefill_status(**kw)
+
+
+@pytest.mark.parametrize("fn", ["kda_checkpoint_write", "kda_checkpoint_restore"])
+def test_copy_host_array_lengths(fn):
+    with pytest.raises(ValueError):
+        getattr(K, fn)(pool(), [1, 2], [3], stream=0)

@@ -5,7 +5,9 @@ section 9.1); identity at beta = 0, alpha = 1; pure decay; exact write at
 beta = 1 (separates the decay-first reading from the literal bracket); the
 outer-product associative memory; the affine composition law and its
 non-commutativity (acpost page, section 1.3); column independence; resume from a
-checkpoint equals the uninterrupted run; checkpoint = state after P tokens.
+checkpoint equals the uninterrupted run; checkpoint = state after P tokens;
+bf16 and fp32 inputs decode exactly (bitwise equal to numpy-widened fp64
+inputs); a head subset equals the matching slices of the all-heads run.
 The mutation test builds the oracle with each planted mistake and requires that
 at least one pin fails for every one of them.
 """
@@ -23,6 +25,9 @@ MUTANTS = {
     6: "checkpoint one token early",
     7: "beta dropped from the write",
     8: "decay applied after the write",
+    9: "bf16 input decoded with one mantissa bit flipped",
+    10: "first selected head used for every selected head",
+    11: "fp32 input truncated to 16 bits",
 }
 
 
