@@ -35,7 +35,7 @@ HASH_BLOCK = 512
 CHUNK = 64
 
 EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset",
-           "kda_prefill_workspace_bytes", "kda_prefill_chunked", "kda_decode_step",
+           "kda_prefill_workspace_bytes", "kda_prefill_workspace_min_bytes", "kda_prefill_chunked", "kda_decode_step",
            "kda_decode_verify",
            "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
            "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8",
@@ -88,6 +88,7 @@ _sig = {
     "kda_pool_check": (ctypes.c_int, [_PP]),
     "kda_state_offset": (_i64, [_PP, _i32, _i32]),
     "kda_prefill_workspace_bytes": (_sz, [_PP, _i64, _i32, _i32, ctypes.c_int]),
+    "kda_prefill_workspace_min_bytes": (_sz, [_PP, _i32, _i32, ctypes.c_int]),
     "kda_prefill_chunked": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
                                            _i32, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, _P, _sz,
                                            _P]),
@@ -240,6 +241,12 @@ def kda_prefill_workspace_bytes(pool: kda_pool, total_tokens: int, num_seqs: int
                                 in_dtype: int) -> int:
     return int(_lib.kda_prefill_workspace_bytes(ctypes.byref(pool), total_tokens, num_seqs,
                                                 num_ckpts, in_dtype))
+
+
+def kda_prefill_workspace_min_bytes(pool: kda_pool, num_seqs: int, num_ckpts: int,
+                                    in_dtype: int) -> int:
+    return int(_lib.kda_prefill_workspace_min_bytes(ctypes.byref(pool), num_seqs, num_ckpts,
+                                                    in_dtype))
 
 
 def kda_prefill_chunked(pool, q, k, v, g, beta, o, cu_seqlens, *, start_pos=None,

@@ -21,6 +21,7 @@
 
 #include "../../include/kda.h"
 #include "kda_launch.h"
+#include "kda_plan.h"
 
 
 using namespace kda;
@@ -45,7 +46,6 @@ kda_status ok() {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // ---- optional per-kernel timing ------------------------------------------
 struct TimedLaunch {
@@ -173,10 +173,19 @@ size_t kda_prefill_workspace_bytes(const kda_pool* pool, int64_t total_tokens, i
   if (check_pool(pool) != KDA_OK || !valid_dtype(in_dtype) || total_tokens < 0 || num_seqs < 0 ||
       num_ckpts < 0)
     return 0;
-  const MetaLayout m = meta_layout(num_seqs, num_ckpts);
+  const int H = pool->num_heads, D = pool->d_k;
+  const PrefillLayout m = prefill_layout(num_seqs, num_ckpts, H, D);
   const int64_t max_chunks = (total_tokens + 63) / 64 + num_seqs;
-  const int64_t blk = inter_block_bytes(pool->d_k, in_dtype == KDA_BF16 ? 2 : 4);
-  return (size_t)(m.inter_off + max_chunks * pool->num_heads * blk);
+  const int64_t wc = std::min<int64_t>(default_window_chunks(H), std::max<int64_t>(max_chunks, 1));
+  return (size_t)(m.inter_off + wc * H * inter_block_bytes(D, in_dtype == KDA_BF16 ? 2 : 4));
+}
+
+size_t kda_prefill_workspace_min_bytes(const kda_pool* pool, int32_t num_seqs, int32_t num_ckpts,
+                                       kda_dtype in_dtype) {
+  if (check_pool(pool) != KDA_OK || !valid_dtype(in_dtype) || num_seqs < 0 || num_ckpts < 0) return 0;
+  const int H = pool->num_heads, D = pool->d_k;
+  const PrefillLayout m = prefill_layout(num_seqs, num_ckpts, H, D);
+  return (size_t)(m.inter_off + (int64_t)H * inter_block_bytes(D, in_dtype == KDA_BF16 ? 2 : 4));
 }
 
 kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* k, const void* v,
@@ -265,20 +274,20 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
     }
   }
   const bool bf = in_dtype == KDA_BF16;
-  const MetaLayout ml = meta_layout(num_seqs, num_ckpts);
+  const PrefillLayout ml = prefill_layout(num_seqs, num_ckpts, H, D);
   const int64_t blk = inter_block_bytes(D, bf ? 2 : 4);
-  const int64_t need = ml.inter_off + total_chunks * H * blk;
   if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((int64_t)workspace_bytes < need)
+  const int32_t wc = fit_window_chunks(ml, H, blk, total_chunks, (int64_t)workspace_bytes);
+  if (wc < 1)
     return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", workspace_bytes,
-                (long long)need);
+                (long long)(ml.inter_off + (int64_t)H * blk));
   if ((int64_t)num_seqs * H > (int64_t)1 << 28) return fail(KDA_ERR_SHAPE, "too many (seq, head) pairs");
   // the kernels address one 64-token chunk of q/k/v/g with 32-bit offsets
   if ((int64_t)H * D > (int64_t)1 << 24) return fail(KDA_ERR_SHAPE, "num_heads * d_k above 2^24");
 
   // ---- metadata tables ------------------------------------------------------
-  std::vector<uint8_t> blob((size_t)ml.inter_off, 0);
+  std::vector<uint8_t> blob((size_t)ml.carry_off, 0);
   SeqEntry* seqs = reinterpret_cast<SeqEntry*>(blob.data() + ml.seq_off);
   int32_t cb = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
@@ -293,22 +302,19 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
     e.ckpt_begin = ckpt_cu ? ckpt_cu[i] : 0;
     e.ckpt_end = ckpt_cu ? ckpt_cu[i + 1] : 0;
   }
-  std::vector<int32_t> order(num_seqs);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int32_t a, int32_t b) { return seqs[a].len > seqs[b].len; });
-  std::memcpy(blob.data() + ml.order_off, order.data(), order.size() * 4);
   CkptEntry* ck = reinterpret_cast<CkptEntry*>(blob.data() + ml.ckpt_off);
   for (int32_t m = 0; m < num_ckpts; ++m) {
     ck[m].pos = ckpt_pos[m];
     ck[m].page = ckpt_page[m];
     ck[m].pad = 0;
   }
+  const std::vector<Window> wins = plan_windows(seqs, num_seqs, total_chunks, wc);
 
   // ---- launches --------------------------------------------------------------
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  // small tables travel inside the kernel arguments (no fill launch)
+  // small tables travel inside the kernel arguments (no fill launch); larger
+  // ones are shipped once, and each window's order table before its scan
   const bool inl = num_seqs <= kInlineSeqs && num_ckpts <= kInlineCkpts;
   if (!inl) {
     s = ship_metadata(ws, blob, st);
@@ -320,23 +326,36 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
   std::memset(&ick, 0, sizeof(ick));
   if (inl) {
     std::memcpy(iseq.e, seqs, sizeof(SeqEntry) * num_seqs);
-    std::memcpy(iseq.order, order.data(), sizeof(int32_t) * num_seqs);
     std::memcpy(ick.e, ck, sizeof(CkptEntry) * num_ckpts);
   }
   uint8_t* inter = ws + ml.inter_off;
-  if (total_chunks > 0) {
-    PrepArgs pa{q, k, g, beta, reinterpret_cast<const SeqEntry*>(ws + ml.seq_off), num_seqs, H,
-                inter, blk, inl ? 1 : 0, 0, iseq};
-    Launch L("kda_prefill_prep", st);
-    hipError_t e = launch_prep(D, bf, pa, (int)total_chunks, st);
-    if (e != hipSuccess) return hip_fail(e, "prep launch");
-  }
-  {
+  float* carry[2] = {reinterpret_cast<float*>(ws + ml.carry_off),
+                     reinterpret_cast<float*>(ws + ml.carry_off) + (int64_t)H * D * D};
+  for (size_t w = 0; w < wins.size(); ++w) {
+    const Window& win = wins[w];
+    if (win.nch > 0) {
+      PrepArgs pa{q, k, g, beta, reinterpret_cast<const SeqEntry*>(ws + ml.seq_off), num_seqs, H,
+                  inter, blk, inl ? 1 : 0, win.c0, iseq};
+      Launch L("kda_prefill_prep", st);
+      hipError_t e = launch_prep(D, bf, pa, win.nch, st);
+      if (e != hipSuccess) return hip_fail(e, "prep launch");
+    }
+    if (win.seqs.empty()) continue;
+    const int32_t nw = (int32_t)win.seqs.size();
+    if (inl) {
+      std::memcpy(iseq.order, win.seqs.data(), sizeof(int32_t) * nw);
+    } else {
+      std::vector<uint8_t> ob((size_t)nw * 4);
+      std::memcpy(ob.data(), win.seqs.data(), ob.size());
+      s = ship_metadata(ws + ml.order_off, ob, st);
+      if (s != KDA_OK) return s;
+    }
     ScanArgs sa{v, o, out_dtype == KDA_BF16, H,
                 reinterpret_cast<const SeqEntry*>(ws + ml.seq_off),
                 reinterpret_cast<const int32_t*>(ws + ml.order_off),
-                reinterpret_cast<const CkptEntry*>(ws + ml.ckpt_off), num_seqs * H, 0, inter, blk,
-                static_cast<uint8_t*>(pool->base), pool->page_bytes, inl ? 1 : 0, 0, iseq, ick};
+                reinterpret_cast<const CkptEntry*>(ws + ml.ckpt_off), nw * H, win.c0, win.nch, 0,
+                inter, blk, static_cast<uint8_t*>(pool->base), pool->page_bytes,
+                carry[w & 1], carry[(w + 1) & 1], inl ? 1 : 0, 0, iseq, ick};
     Launch L("kda_prefill_scan", st);
     hipError_t e = launch_scan(D, bf, sa, st);
     if (e != hipSuccess) return hip_fail(e, "scan launch");

@@ -15,7 +15,7 @@ constexpr int kInlineSeqs = 16;
 constexpr int kInlineCkpts = 64;
 struct InlineSeqs {
   SeqEntry e[kInlineSeqs];
-  int32_t order[kInlineSeqs];  // sequences by descending length
+  int32_t order[kInlineSeqs];  // the window's sequences by descending chunk count
 };
 struct InlineCkpts {
   CkptEntry e[kInlineCkpts];
@@ -29,27 +29,35 @@ struct PrepArgs {
   const SeqEntry* seqs;  // workspace table (when !inline_meta)
   int32_t num_seqs;
   int32_t H;
-  uint8_t* inter;
+  uint8_t* inter;         // block of chunk c, head h at ((c - chunk0) * H + h) * blk_bytes
   int64_t blk_bytes;
   int32_t inline_meta;
-  int32_t pad;
+  int32_t chunk0;         // first global chunk of the window
   InlineSeqs iseq;
 };
 
+// One window of a prefill call: global chunks [c0, c0 + nch).  Each of its
+// sequences runs the part of its chunks inside the window; a sequence that
+// began in an earlier window enters with the carried state (carry_in), one
+// that continues past the window leaves its state in carry_out.
 struct ScanArgs {
   const void* v;
   void* o;
   int32_t out_bf16;
   int32_t H;
   const SeqEntry* seqs;
-  const int32_t* order;  // sequences by descending length
+  const int32_t* order;  // the window's sequences by descending chunk count
   const CkptEntry* ckpts;
-  int32_t npairs;  // num_seqs * H
+  int32_t npairs;  // (sequences in the window) * H
+  int32_t c0;      // first global chunk of the window
+  int32_t nch;     // chunks in the window
   int32_t pad;
   const uint8_t* inter;
   int64_t blk_bytes;
   uint8_t* pool;
   int64_t page_bytes;
+  const float* carry_in;  // [H][D][D] fp32
+  float* carry_out;       // [H][D][D] fp32 (never the same buffer as carry_in)
   int32_t inline_meta;
   int32_t pad2;
   InlineSeqs iseq;

@@ -130,7 +130,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // chunks in reverse dispatch order (see prep2_kernel)
-  const int chunk = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, H = a.H;
+  const int wchunk = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, H = a.H;
+  const int chunk = a.chunk0 + wchunk;
   const SeqEntry se = seq_at(a, find_seq_in(a, chunk));
   const int lc = chunk - se.chunk_begin;
   const int64_t row0 = se.row_begin + 64LL * lc;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const Op* gk = reinterpret_cast<const Op*>(a.k);
   const Op* gg = reinterpret_cast<const Op*>(a.g);
   const Op* gb = reinterpret_cast<const Op*>(a.beta);
-  Op* out = reinterpret_cast<Op*>(a.inter + ((int64_t)chunk * H + h) * a.blk_bytes);
+  Op* out = reinterpret_cast<Op*>(a.inter + ((int64_t)wchunk * H + h) * a.blk_bytes);
   using IO = InterOff<D>;
   constexpr int CG = D / 8;
 
@@ -348,8 +349,9 @@ __device__ __forceinline__ void prep2_load(const PrepArgs& a, int pair, int t, P
   // would wait on every store still in flight; the table is not written
   // while the kernel runs)
   const int H = a.H;
-  const int chunk = __builtin_amdgcn_readfirstlane(pair / H);
-  const int h = __builtin_amdgcn_readfirstlane(pair - chunk * H);
+  const int wchunk = __builtin_amdgcn_readfirstlane(pair / H);
+  const int h = __builtin_amdgcn_readfirstlane(pair - wchunk * H);
+  const int chunk = a.chunk0 + wchunk;
   const SeqEntry se = seq_at(a, find_seq_in(a, chunk));
   const int lc = chunk - se.chunk_begin;
   const int64_t row0 = se.row_begin + 64LL * lc;
@@ -437,8 +439,8 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
     }
   }
   const int H = a.H;
-  const int chunk = pair / H, h = pair - (pair / H) * H;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.inter + ((int64_t)chunk * H + h) * a.blk_bytes);
+  const int wchunk = pair / H, h = pair - (pair / H) * H;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.inter + ((int64_t)wchunk * H + h) * a.blk_bytes);
   if (it != (int)blockIdx.x) __syncthreads();  // the previous pair is done with LDS
   if (t < 64) beta_s[t] = t < len ? bf16_to_f32(in.beta) : 0.f;
 
@@ -737,6 +739,7 @@ struct ScanCtx {
 // the waves compute instead of stalling them all at the top of the chunk.
 template <int D, typename Op>
 __device__ __forceinline__ const Op* chunk_block(const ScanCtx& c, int n) {
+  // chunk_begin is relative to the window's first chunk
   return reinterpret_cast<const Op*>(c.inter +
                                      ((int64_t)(c.chunk_begin + n) * c.H + c.h) * c.blk_bytes);
 }
@@ -833,29 +836,35 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   c.owns_s = 16 * wv < D;
   c.row_begin = se.row_begin;
   c.len = se.len;
-  c.chunk_begin = se.chunk_begin;
+  c.chunk_begin = se.chunk_begin - a.c0;
   const int rt = wv & 3;
   const int64_t hoff = (int64_t)h * D * D;
   const int nchunks = (se.len + 63) / 64;
+  // the sequence's chunks inside this window: [n_lo, n_hi)
+  const int n_lo = max(a.c0 - se.chunk_begin, 0);
+  const int n_hi = min(a.c0 + a.nch - se.chunk_begin, nchunks);
 
   CO f0, f1, f2, f3;
-  if (nchunks > 0) {
-    load_ops<D, Op, NH>(f0, c, 0);
-    if (PF >= 2) load_ops<D, Op, NH>(f1, c, min(1, nchunks - 1));
-    if (PF >= 3) load_ops<D, Op, NH>(f2, c, min(2, nchunks - 1));
+  if (n_hi > n_lo) {
+    load_ops<D, Op, NH>(f0, c, n_lo);
+    if (PF >= 2) load_ops<D, Op, NH>(f1, c, min(n_lo + 1, n_hi - 1));
+    if (PF >= 3) load_ops<D, Op, NH>(f2, c, min(n_lo + 2, n_hi - 1));
   }
 
-  // this wave's S tiles: rows 16*wv + 4*(lane/16) + r, column c0 + 16*j + lane%16
+  // this wave's S tiles: rows 16*wv + 4*(lane/16) + r, column c0 + 16*j + lane%16;
+  // the entering state is the sequence's (first window) or the carried one
   f32x4 S[NH];
 #pragma unroll
   for (int j = 0; j < NH; ++j) S[j] = zero4();
-  if (c.owns_s && se.state_in >= 0) {
-    const float* src = reinterpret_cast<const float*>(a.pool + se.state_in * a.page_bytes) + hoff;
+  const float* s_src = n_lo > 0 ? a.carry_in + hoff
+                       : se.state_in >= 0 ? reinterpret_cast<const float*>(a.pool + se.state_in * a.page_bytes) + hoff
+                                          : nullptr;
+  if (c.owns_s && s_src) {
 #pragma unroll
     for (int j = 0; j < NH; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        S[j][r] = src[(16 * wv + acc_row(lane, r)) * D + c.c0 + 16 * j + acc_col(lane)];
+        S[j][r] = s_src[(16 * wv + acc_row(lane, r)) * D + c.c0 + 16 * j + acc_col(lane)];
   }
   auto s_to_lds = [&]() {
     if (c.owns_s) {
@@ -869,9 +878,8 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
       }
     }
   };
-  auto s_store = [&](int page) {
+  auto s_store_to = [&](float* dst) {
     if (c.owns_s) {
-      float* dst = reinterpret_cast<float*>(a.pool + page * a.page_bytes) + hoff;
 #pragma unroll
       for (int j = 0; j < NH; ++j)
 #pragma unroll
@@ -879,6 +887,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
           dst[(16 * wv + acc_row(lane, r)) * D + c.c0 + 16 * j + acc_col(lane)] = S[j][r];
     }
   };
+  auto s_store = [&](int page) { s_store_to(reinterpret_cast<float*>(a.pool + page * a.page_bytes) + hoff); };
   s_to_lds();
 
   int nck = se.ckpt_begin;
@@ -887,10 +896,12 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   const ConstCkptPtr ck = (ConstCkptPtr)(a.ckpts);
   auto ck_pos = [&](int i) -> int64_t { return a.inline_meta ? a.ick.e[i].pos : ck[i].pos; };
   auto ck_page = [&](int i) -> int { return a.inline_meta ? a.ick.e[i].page : ck[i].page; };
+  // checkpoints at or before the window's first token belong to earlier windows
+  while (nck < se.ckpt_end && ck_pos(nck) <= se.start_pos + 64LL * n_lo) ++nck;
   int64_t next_pos = nck < se.ckpt_end ? ck_pos(nck) : -1;
 
   auto step = [&](CO& cur, CO& pre, int n) {
-    const int nf = min(n + PF, nchunks - 1);  // chunk whose operands are prefetched
+    const int nf = min(n + PF, n_hi - 1);  // chunk whose operands are prefetched (inside the window)
     load_ops_a<D, Op, NH>(pre, c, nf);
     __builtin_amdgcn_sched_barrier(0);
     const int len = min(64, se.len - 64 * n);
@@ -1015,27 +1026,28 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
     s_to_lds();
   };
 
-  int n = 0;
+  int n = n_lo;
   if constexpr (PF == 3) {
-    for (; n + 4 <= nchunks; n += 4) {
+    for (; n + 4 <= n_hi; n += 4) {
       step(f0, f3, n);
       step(f1, f0, n + 1);
       step(f2, f1, n + 2);
       step(f3, f2, n + 3);
     }
-    if (n < nchunks) step(f0, f3, n);
-    if (n + 1 < nchunks) step(f1, f0, n + 1);
-    if (n + 2 < nchunks) step(f2, f1, n + 2);
+    if (n < n_hi) step(f0, f3, n);
+    if (n + 1 < n_hi) step(f1, f0, n + 1);
+    if (n + 2 < n_hi) step(f2, f1, n + 2);
   } else {
-    for (; n + 2 <= nchunks; n += 2) {
+    for (; n + 2 <= n_hi; n += 2) {
       step(f0, f1, n);
       step(f1, f0, n + 1);
     }
-    if (n < nchunks) step(f0, f1, n);
+    if (n < n_hi) step(f0, f1, n);
   }
   (void)f2;
   (void)f3;
-  if (se.state_out >= 0) s_store(se.state_out);
+  if (n_hi < nchunks) s_store_to(a.carry_out + hoff);  // continues in the next window
+  else if (se.state_out >= 0) s_store(se.state_out);
 }
 
 // ---------------------------------------------------------------------------

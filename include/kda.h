@@ -115,14 +115,27 @@ kda_status kda_pool_check(const kda_pool* pool);
 int64_t kda_state_offset(const kda_pool* pool, int32_t page, int32_t head);
 
 /*
- * Device workspace bytes kda_prefill_chunked needs for a call with these
+ * Device workspace bytes kda_prefill_chunked prefers for a call with these
  * sizes (total_tokens = cu_seqlens[num_seqs], num_ckpts = ckpt_cu[num_seqs]).
  * Returns 0 for invalid arguments.  The workspace holds the call's metadata
- * tables and the per-(chunk, head) intermediates of the chunk form; it must be
- * 256-byte aligned and is free for reuse once the stream passes the call.
+ * tables, two carried states (H heads each) and one window of the call: the
+ * per-(chunk, head) intermediates of the chunk form for up to
+ * max(1, 2048 / H) consecutive 64-token chunks (about 135 MB at H = 32,
+ * d = 128, bf16), whatever the length of the call.  It must be 256-byte
+ * aligned and is free for reuse once the stream passes the call.
  */
 size_t kda_prefill_workspace_bytes(const kda_pool* pool, int64_t total_tokens, int32_t num_seqs,
                                    int32_t num_ckpts, kda_dtype in_dtype);
+
+/*
+ * The smallest workspace kda_prefill_chunked accepts for num_seqs sequences
+ * and num_ckpts checkpoints, of any length: windows of one chunk.  Any size
+ * from this one up is accepted; the call uses the largest window (up to the
+ * preferred one) that fits, so a smaller workspace means more launches,
+ * never different results.  Returns 0 for invalid arguments.
+ */
+size_t kda_prefill_workspace_min_bytes(const kda_pool* pool, int32_t num_seqs, int32_t num_ckpts,
+                                       kda_dtype in_dtype);
 
 /*
  * Chunk-parallel prefill of a packed batch of sequences [ARCH][AFF], with the
@@ -152,7 +165,12 @@ size_t kda_prefill_workspace_bytes(const kda_pool* pool, int64_t total_tokens, i
  *                  checkpoint at P is the state after P tokens.
  *   ckpt_page      destination page of each checkpoint (a fresh page).
  * chunk_size must be 64; hash_block a positive multiple of 64 (512 in the
- * pages).  workspace must hold kda_prefill_workspace_bytes(...) bytes.
+ * pages).  workspace must hold at least kda_prefill_workspace_min_bytes(...)
+ * bytes (KDA_ERR_WORKSPACE otherwise).
+ * Windows: the call runs in windows of consecutive chunks of the packed batch
+ * (prep of the window's chunks, then the scan of the sequences owning them); a
+ * sequence cut by a window edge carries its fp32 state across unchanged, so
+ * the results are bit-identical for every workspace size.
  * Destination pages (state_out_page, ckpt_page) must be distinct and must not
  * be any state_in_page, apart from the in-place case above (KDA_ERR_PAGE_ALIAS).
  *

@@ -89,8 +89,13 @@ def test_workspace_bytes():
     assert a > 0 and b > a
     # per (chunk, head): 3 x [64][128] + 2 x [64][64] elements + fp32 gamma, 256-aligned
     blk = ((3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128 + 255) // 256 * 256
-    assert a >= (8192 // 64) * 32 * blk
-    assert K.kda_prefill_workspace_bytes(p, 8192, 2, 3, K.KDA_BF16) > a
+    assert a >= 64 * 32 * blk  # one window of 64 chunks
+    assert K.kda_prefill_workspace_bytes(p, 8192, 2, 3, K.KDA_BF16) >= a
+    # the workspace holds one window (2048 (chunk, head) blocks), not the
+    # whole call: a 1M-token call needs no more than an 8K one
+    big = K.kda_prefill_workspace_bytes(p, 1 << 20, 1, 170, K.KDA_BF16)
+    assert big <= a + 4096 and big < 1 << 30
+    assert K.kda_prefill_workspace_bytes(p, 64, 1, 0, K.KDA_BF16) < a // 16  # short calls stay small
     assert K.kda_prefill_workspace_bytes(p, -1, 1, 0, K.KDA_BF16) == 0
     assert K.kda_prefill_workspace_bytes(p, 10, 1, 0, 7) == 0
 
@@ -155,16 +160,22 @@ def test_prefill_rejects_bad_pool_and_accepts_empty_batch():
 
 
 def test_workspace_bound_matches_check():
-    """The size kda_prefill_workspace_bytes reports is accepted; one byte less
-    than the exact need is rejected (varlen, partial chunks)."""
+    """The preferred size (kda_prefill_workspace_bytes) covers the smallest one
+    (kda_prefill_workspace_min_bytes: one chunk per window); one byte less than
+    the smallest is rejected by the call's validation (varlen, partial chunks)."""
     p = pool()
     cu = [0, 100, 100, 1000, 1100]
-    need = K.kda_prefill_workspace_bytes(p, 1100, 4, 0, K.KDA_BF16)
-    chunks = sum((b - a + 63) // 64 for a, b in zip(cu[:-1], cu[1:]))
+    pref = K.kda_prefill_workspace_bytes(p, 1100, 4, 0, K.KDA_BF16)
+    least = K.kda_prefill_workspace_min_bytes(p, 4, 0, K.KDA_BF16)
+    assert 0 < least <= pref
+    # one window of one chunk: 32 heads of (chunk, head) blocks, plus two
+    # carried states of 32 heads
     blk = ((3 * 64 * 128 + 2 * 64 * 64) * 2 + 4 * 128 + 255) // 256 * 256
-    exact_inter = chunks * 32 * blk
-    assert need >= exact_inter
-    assert _prefill_status(p=p, cu_seqlens=cu, workspace_bytes=exact_inter - 1) == K.KDA_ERR_WORKSPACE
+    assert least >= 32 * blk + 2 * 32 * 65536
+    chunks = sum((b - a + 63) // 64 for a, b in zip(cu[:-1], cu[1:]))
+    assert pref >= least + (chunks - 1) * 32 * blk  # the whole call fits one window
+    assert _prefill_status(p=p, cu_seqlens=cu, workspace_bytes=least - 1) == K.KDA_ERR_WORKSPACE
+    assert K.kda_prefill_workspace_min_bytes(p, -1, 0, K.KDA_BF16) == 0
 
 
 @pytest.mark.parametrize("fn", ["kda_checkpoint_write", "kda_checkpoint_restore"])

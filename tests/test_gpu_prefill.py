@@ -321,6 +321,78 @@ def test_slab_width_bitwise(dtype, monkeypatch):
     assert np.array_equal(res[0][1], res[1][1])
 
 
+@pytest.mark.parametrize("dtype,nseq", [("bf16", 4), ("f32", 4), ("bf16", 20)])
+def test_window_size_bitwise(dtype, nseq):
+    """A call runs in windows of consecutive chunks that fit the workspace it is
+    given.  The preferred workspace, the smallest accepted one (one chunk per
+    window) and one of three chunks per window give bit-identical o,
+    checkpoints and final states: a sequence cut by a window edge carries its
+    fp32 state across unchanged.  Covers resumed sequences, an empty sequence
+    with a state, checkpoints on window edges and inside windows, and (20
+    sequences) the tables shipped through the workspace rather than inline.
+    The preferred run matches the oracle."""
+    H, D = 4, 128
+    rng = np.random.default_rng(nseq)
+    if nseq == 4:
+        lens = [2500, 0, 1600, 900]
+    else:
+        lens = [int(x) for x in rng.integers(1, 700, nseq)]
+        lens[1] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    sp = [64 * int(x) for x in rng.integers(0, 20, nseq)]
+    sp[0] = 0
+    s_in = [-1] * nseq
+    s_in[1], s_in[2] = 2 * nseq, 2 * nseq + 1
+    s_out = list(range(nseq))
+    ck_cu, ck_pos, ck_page = [0], [], []
+    for i in range(nseq):
+        for pos in range((sp[i] // 512 + 1) * 512, sp[i] + lens[i] + 1, 512):
+            ck_pos.append(pos)
+            ck_page.append(2 * nseq + 2 + len(ck_page))
+        ck_cu.append(len(ck_pos))
+    nck = len(ck_pos)
+    npages = 2 * nseq + 2 + nck
+    d = G.kda_tokens(2024 + nseq, H, D, 0, int(cu[-1]), dtype)
+    di = inputs_to_dev(d, dtype)
+    ind = K.KDA_BF16 if dtype == "bf16" else K.KDA_F32
+    pool0 = PoolBuf(npages, H, D).pool
+    full = K.kda_prefill_workspace_bytes(pool0, int(cu[-1]), nseq, nck, ind)
+    small = K.kda_prefill_workspace_min_bytes(pool0, nseq, nck, ind)
+    op = 2 if dtype == "bf16" else 4
+    blk = ((3 * 64 * D + 2 * 64 * 64) * op + 4 * D + 255) // 256 * 256  # one (chunk, head) block
+    assert 0 < small < full // 4, (small, full)
+    s0 = (np.random.default_rng(3).standard_normal((2, H, D, D)) / np.sqrt(D)).astype(np.float32)
+    res = []
+    for nbytes in (full, small, small + 2 * H * blk):
+        pb = PoolBuf(npages, H, D)
+        pb.set_states(2 * nseq, s0[0])
+        pb.set_states(2 * nseq + 1, s0[1])
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        o = torch.full((int(cu[-1]), H, D), float("nan"), device="cuda",
+                       dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+        K.kda_prefill_chunked(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, cu,
+                              start_pos=sp, state_in_page=s_in, state_out_page=s_out, workspace=ws,
+                              ckpt_cu=ck_cu, ckpt_pos=ck_pos, ckpt_page=ck_page)
+        torch.cuda.synchronize()
+        res.append(((o.view(torch.int16) if dtype == "bf16" else o.view(torch.int32)).cpu().numpy(),
+                    pb.snapshot(), o.double().cpu().numpy(), pb))
+    for r in res[1:]:
+        assert np.array_equal(res[0][0], r[0])
+        assert np.array_equal(res[0][1], r[1])
+    s0_in = np.zeros((nseq, H, D, D))
+    s0_in[1], s0_in[2] = s0[0], s0[1]
+    ref = _oracle_prefill(d, cu, start_pos=sp, s0=s0_in, ckpt_cu=ck_cu, ckpt_pos=ck_pos)
+    pb = res[0][3]
+    err = max_rel_blocks(res[0][2], ref["o"], cu, H)
+    for m, p in enumerate(ck_page):
+        err = max(err, max(rel_fro(pb.states(p)[h], ref["ckpts"][m, h]) for h in range(H)))
+    for s_, p in enumerate(s_out):
+        if lens[s_] > 0 or s_in[s_] >= 0:
+            err = max(err, max(rel_fro(pb.states(p)[h], ref["s_final"][s_, h]) for h in range(H)))
+    assert np.array_equal(pb.states(s_out[1]), s0_in[1])  # the empty sequence keeps its state
+    assert err <= TOL[dtype], err
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_unwritten_workspace_never_read(dtype, D):
     """Workspace bytes that a call does not write (the zero fragments of the
