@@ -35,8 +35,8 @@ HASH_BLOCK = 512
 CHUNK = 64
 
 EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset",
-           "kda_prefill_workspace_bytes", "kda_prefill_workspace_min_bytes", "kda_prefill_chunked", "kda_decode_step",
-           "kda_decode_verify",
+           "kda_prefill_workspace_bytes", "kda_prefill_workspace_min_bytes", "kda_prefill_chunked",
+           "kda_prefill_chunked_noalloc", "kda_decode_step", "kda_decode_verify",
            "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
            "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8",
            "kda_conv_workspace_bytes", "kda_short_conv", "kda_profile_enable", "kda_profile_read",
@@ -92,6 +92,9 @@ _sig = {
     "kda_prefill_chunked": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
                                            _i32, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, _P, _sz,
                                            _P]),
+    "kda_prefill_chunked_noalloc": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P,
+                                                    ctypes.c_int, _i32, _P, _P, _P, _P, _P, _P, _P,
+                                                    _i32, _i32, _P]),
     "kda_decode_step": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
                                        _i32, _P, _P, _P]),
     "kda_decode_verify": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int,
@@ -274,6 +277,30 @@ def kda_prefill_chunked(pool, q, k, v, g, beta, o, cu_seqlens, *, start_pos=None
                                   _dptr(beta), ind, _dptr(o), outd, ns, cu.ptr, sp.ptr, si.ptr,
                                   so.ptr, ccu.ptr, cpos.ptr, cpg.ptr, chunk_size, hash_block,
                                   _dptr(workspace), workspace_bytes, _stream(stream))
+    _check(st)
+
+
+def kda_prefill_chunked_noalloc(pool, q, k, v, g, beta, o, cu_seqlens, *, start_pos=None,
+                                state_in_page=None, state_out_page=None, ckpt_cu=None,
+                                ckpt_pos=None, ckpt_page=None, chunk_size=CHUNK,
+                                hash_block=HASH_BLOCK, in_dtype=None, out_dtype=None, stream=None):
+    """kda_prefill_chunked on the library's static device scratch (no workspace
+    argument; see include/kda.h)."""
+    cu = _HostArr(cu_seqlens, np.int64)
+    ns = len(cu.a) - 1
+    sp = _HostArr(start_pos, np.int64)
+    si = _HostArr(state_in_page, np.int32)
+    so = _HostArr(state_out_page, np.int32)
+    ccu = _HostArr(ckpt_cu, np.int32)
+    cpos = _HostArr(ckpt_pos, np.int64)
+    cpg = _HostArr(ckpt_page, np.int32)
+    _seq_meta_lengths(ns, sp, si, so, ccu, cpos, cpg)
+    ind = _dtype_code(q) if in_dtype is None else in_dtype
+    outd = _dtype_code(o) if out_dtype is None else out_dtype
+    st = _lib.kda_prefill_chunked_noalloc(ctypes.byref(pool), _dptr(q), _dptr(k), _dptr(v),
+                                          _dptr(g), _dptr(beta), ind, _dptr(o), outd, ns, cu.ptr,
+                                          sp.ptr, si.ptr, so.ptr, ccu.ptr, cpos.ptr, cpg.ptr,
+                                          chunk_size, hash_block, _stream(stream))
     _check(st)
 
 

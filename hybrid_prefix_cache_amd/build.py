@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_copy.hip", "kda_ckpt_int8.hip", "kda_conv.hip",
-           "kda_index.cpp"]
+           "kda_index.cpp", "kda_noalloc.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          # no packed fp32 instructions (v_pk_*_f32) in device code

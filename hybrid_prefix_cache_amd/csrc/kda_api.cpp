@@ -188,14 +188,20 @@ size_t kda_prefill_workspace_min_bytes(const kda_pool* pool, int32_t num_seqs, i
   return (size_t)(m.inter_off + (int64_t)H * inter_block_bytes(D, in_dtype == KDA_BF16 ? 2 : 4));
 }
 
-kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* k, const void* v,
-                               const void* g, const void* beta, kda_dtype in_dtype, void* o,
-                               kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
-                               const int64_t* start_pos, const int32_t* state_in_page,
-                               const int32_t* state_out_page, const int32_t* ckpt_cu,
-                               const int64_t* ckpt_pos, const int32_t* ckpt_page,
-                               int32_t chunk_size, int32_t hash_block, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// The chunked prefill.  With `scratch` set, `workspace` is ignored: once the
+// call has passed validation, scratch() supplies the workspace (the library's
+// static device array, workspace_bytes long) and a call that does not fit it
+// is rejected as such.
+kda_status kda::prefill_impl(const kda_pool* pool, const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                             kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
+                             const int64_t* start_pos, const int32_t* state_in_page,
+                             const int32_t* state_out_page, const int32_t* ckpt_cu,
+                             const int64_t* ckpt_pos, const int32_t* ckpt_page, int32_t chunk_size,
+                             int32_t hash_block, void* workspace, size_t workspace_bytes,
+                             kda_status (*scratch)(void**), void* stream) {
   kda_status s = check_pool(pool);
   if (s != KDA_OK) return s;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
@@ -276,15 +282,24 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
   const bool bf = in_dtype == KDA_BF16;
   const PrefillLayout ml = prefill_layout(num_seqs, num_ckpts, H, D);
   const int64_t blk = inter_block_bytes(D, bf ? 2 : 4);
-  if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const int32_t wc = fit_window_chunks(ml, H, blk, total_chunks, (int64_t)workspace_bytes);
-  if (wc < 1)
-    return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", workspace_bytes,
-                (long long)(ml.inter_off + (int64_t)H * blk));
   if ((int64_t)num_seqs * H > (int64_t)1 << 28) return fail(KDA_ERR_SHAPE, "too many (seq, head) pairs");
   // the kernels address one 64-token chunk of q/k/v/g with 32-bit offsets
   if ((int64_t)H * D > (int64_t)1 << 24) return fail(KDA_ERR_SHAPE, "num_heads * d_k above 2^24");
+  const int32_t wc = fit_window_chunks(ml, H, blk, total_chunks, (int64_t)workspace_bytes);
+  if (wc < 1) {
+    const long long least = (long long)(ml.inter_off + (int64_t)H * blk);
+    if (scratch)
+      return fail(KDA_ERR_WORKSPACE,
+                  "the call needs %lld bytes of workspace, above the static scratch of %zu bytes "
+                  "(fewer sequences, checkpoints or heads per call)", least, workspace_bytes);
+    return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu < %lld bytes", workspace_bytes, least);
+  }
+  if (scratch) {
+    s = scratch(&workspace);
+    if (s != KDA_OK) return s;
+  }
+  if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
   // ---- metadata tables ------------------------------------------------------
   std::vector<uint8_t> blob((size_t)ml.carry_off, 0);
@@ -361,6 +376,21 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
     if (e != hipSuccess) return hip_fail(e, "scan launch");
   }
   return ok();
+}
+
+extern "C" {
+
+kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                               kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
+                               const int64_t* start_pos, const int32_t* state_in_page,
+                               const int32_t* state_out_page, const int32_t* ckpt_cu,
+                               const int64_t* ckpt_pos, const int32_t* ckpt_page,
+                               int32_t chunk_size, int32_t hash_block, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return prefill_impl(pool, q, k, v, g, beta, in_dtype, o, out_dtype, num_seqs, cu_seqlens,
+                      start_pos, state_in_page, state_out_page, ckpt_cu, ckpt_pos, ckpt_page,
+                      chunk_size, hash_block, workspace, workspace_bytes, nullptr, stream);
 }
 
 static kda_status decode_impl(const char* what, const kda_pool* pool, const void* q, const void* k,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/kda.h"
 #include "kda_meta.h"
 
 namespace kda {
@@ -184,6 +185,18 @@ struct ConvArgs {
   int32_t out_bf16;
   int32_t hash_block;
 };
+
+// The chunked prefill behind kda_prefill_chunked (scratch == nullptr) and
+// kda_prefill_chunked_noalloc (scratch supplies the static workspace after
+// validation).
+kda_status prefill_impl(const kda_pool* pool, const void* q, const void* k, const void* v,
+                        const void* g, const void* beta, kda_dtype in_dtype, void* o,
+                        kda_dtype out_dtype, int32_t num_seqs, const int64_t* cu_seqlens,
+                        const int64_t* start_pos, const int32_t* state_in_page,
+                        const int32_t* state_out_page, const int32_t* ckpt_cu,
+                        const int64_t* ckpt_pos, const int32_t* ckpt_page, int32_t chunk_size,
+                        int32_t hash_block, void* workspace, size_t workspace_bytes,
+                        kda_status (*scratch)(void**), void* stream);
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t st);
 hipError_t launch_conv(const ConvArgs& a, int32_t total_chunks, hipStream_t st);

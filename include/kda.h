@@ -192,6 +192,36 @@ kda_status kda_prefill_chunked(const kda_pool* pool, const void* q, const void* 
                                int32_t chunk_size, int32_t hash_block, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Size of the static device scratch behind kda_prefill_chunked_noalloc. */
+#define KDA_PREFILL_SCRATCH_BYTES (64u << 20)
+
+/*
+ * kda_prefill_chunked without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not allocate, harnesses that forbid allocation).  Arguments, results,
+ * validation and errors are those of kda_prefill_chunked; the workspace is a
+ * static device array of KDA_PREFILL_SCRATCH_BYTES (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  The call allocates
+ * nothing: the array's device address is resolved once per device (on the
+ * first call on that device, which must be the current one).  Any length is
+ * accepted (the call runs in windows that fit the array; results are
+ * bit-identical to kda_prefill_chunked); a call whose tables and one window
+ * of one chunk do not fit, i.e. kda_prefill_workspace_min_bytes(...) >
+ * KDA_PREFILL_SCRATCH_BYTES, is rejected with KDA_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU uses the same array, and each
+ * call writes every scratch byte it reads, so nothing needs clearing between
+ * calls; calls that overlap on one GPU (different streams, or host threads
+ * without ordering) race on the array and must be serialised by the caller.
+ */
+kda_status kda_prefill_chunked_noalloc(const kda_pool* pool, const void* q, const void* k,
+                                       const void* v, const void* g, const void* beta,
+                                       kda_dtype in_dtype, void* o, kda_dtype out_dtype,
+                                       int32_t num_seqs, const int64_t* cu_seqlens,
+                                       const int64_t* start_pos, const int32_t* state_in_page,
+                                       const int32_t* state_out_page, const int32_t* ckpt_cu,
+                                       const int64_t* ckpt_pos, const int32_t* ckpt_page,
+                                       int32_t chunk_size, int32_t hash_block, void* stream);
+
 /*
  * One decode step for n requests [ARCH][AFF 2.1]: for each request r and head
  * h, read S from page_in[r], apply one token (q, k, v, g, beta of row r), write

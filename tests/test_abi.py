@@ -178,6 +178,29 @@ def test_workspace_bound_matches_check():
     assert K.kda_prefill_workspace_min_bytes(p, -1, 0, K.KDA_BF16) == 0
 
 
+def test_noalloc_rejects_calls_above_the_static_scratch():
+    """kda_prefill_chunked_noalloc rejects, before any device access, a call
+    whose tables and one-chunk window exceed its static scratch (512 heads:
+    two carried states alone are 64 MiB), and passes invalid calls to the
+    full validation."""
+    p = pool(num_heads=512, page_bytes=512 * 65536)
+    need = K.kda_prefill_workspace_min_bytes(p, 1, 0, K.KDA_BF16)
+    assert need > 64 << 20
+    for kw, status in ((dict(), K.KDA_ERR_WORKSPACE), (dict(in_dtype=9), K.KDA_ERR_DTYPE)):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE, in_dtype=K.KDA_BF16,
+                    out_dtype=K.KDA_BF16, stream=0)
+        args.update(kw)
+        with pytest.raises(K.KdaError) as e:
+            K.kda_prefill_chunked_noalloc(p, cu_seqlens=[0, 1024], **args)
+        assert e.value.status == status
+        assert "static scratch" in K.kda_last_error() or status != K.KDA_ERR_WORKSPACE
+    with pytest.raises(K.KdaError) as e:
+        K.kda_prefill_chunked_noalloc(pool(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, [0, 1024],
+                                      chunk_size=32, in_dtype=K.KDA_BF16, out_dtype=K.KDA_BF16,
+                                      stream=0)
+    assert e.value.status == K.KDA_ERR_SHAPE
+
+
 @pytest.mark.parametrize("fn", ["kda_checkpoint_write", "kda_checkpoint_restore"])
 @pytest.mark.parametrize("src,dst,status", [
     ([1, 2], [3, 16], K.KDA_ERR_PAGE_RANGE),
