@@ -107,7 +107,8 @@ template <int D> struct PrepLayout {
   static constexpr int kR0Bytes = (64 * D * 4 > 2 * 64 * LDF * 4) ? 64 * D * 4 : 2 * 64 * LDF * 4;
   static constexpr int kY = kR0 + kR0Bytes;     // fp32 [3][16][17]
   static constexpr int kBeta = kY + 3 * 16 * 17 * 4;  // fp32 [64]
-  static constexpr int kBytes = kBeta + 64 * 4;
+  static constexpr int kEM = kBeta + 64 * 4;          // fp32 [D]: exp(G_31) per channel
+  static constexpr int kBytes = kEM + D * 4;
   static_assert(kBytes <= 160 * 1024, "prep LDS budget");
 };
 
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   float* Ti = Gm + 64 * LDF;                              // [64][LDF] inverse, then T (fp32)
   float* Y = reinterpret_cast<float*>(smem + LY::kY);
   float* beta_s = reinterpret_cast<float*>(smem + LY::kBeta);
+  float* em_s = reinterpret_cast<float*>(smem + LY::kEM);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // chunks in reverse dispatch order (see prep2_kernel)
@@ -173,6 +175,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   }
 
   // ---- phase 2: decayed tiles ------------------------------------------------
+  // The Gram tiles (LDS) take the mid-chunk prefix G_31 as reference:
+  // Kt' = K exp(G - G_31), Kh' = K exp(G_31 - G), Qt' = Q exp(G - G_31)
+  // (exp(G_i - G_j) K_i K_j per channel as with any reference, each factor
+  // within exp(+-(half a chunk of gates))).  The workspace pieces keep the
+  // chunk-start reference, where every factor is at most 1: Qt = Q exp(G),
+  // Kend = K exp(G_C - G); Keff = T Kt' diag(exp(G_31)) (phase 5).
   for (int it = tid; it < 64 * CG; it += 256) {
     const int r = it / CG, cg = it % CG, c0 = 8 * cg;
     float kx[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -183,13 +191,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     float kt[8], kh[8], qt[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float G = Gm[r * D + c0 + j], GC = Gm[63 * D + c0 + j];
-      const float e = __expf(G), ei = __expf(-G), eci = __expf(GC - G);
+      const float G = Gm[r * D + c0 + j], GC = Gm[63 * D + c0 + j], GM = Gm[31 * D + c0 + j];
+      const float e = __expf(G - GM), ei = __expf(GM - G), eci = __expf(GC - G);
       kt[j] = kx[j] * e;
       kh[j] = kx[j] * ei;
       qt[j] = qx[j] * e;
       out[IO::kKendT + frag_off<KK>(c0 + j, r, 64)] = OT::from_f(kx[j] * eci);
-      out[IO::kQt + frag_off<KK>(r, c0 + j, D)] = OT::from_f(qt[j]);
+      out[IO::kQt + frag_off<KK>(r, c0 + j, D)] = OT::from_f(qx[j] * __expf(G));
     }
     store8(Kt + r * LDK + c0, kt);
     store8(Kh + r * LDK + c0, kh);
@@ -198,6 +206,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   if (tid < D) {
     float* gamma = reinterpret_cast<float*>(out + IO::kGammaElems);
     gamma[tid] = __expf(Gm[63 * D + tid]);
+    em_s[tid] = __expf(Gm[31 * D + tid]);
   }
   __syncthreads();
 
@@ -277,10 +286,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     for (int nt = 0; nt < D / 16; ++nt) {
       f32x4 acc = zero4();
       tile_mma_kn(acc, Ti, LDF, 16 * mt, reinterpret_cast<const float*>(Kt), LDK, 16 * nt, 0, ke, lane);
+      const float em = em_s[16 * nt + acc_col(lane)];  // back to the chunk-start reference
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * mt + acc_row(lane, r), j = 16 * nt + acc_col(lane);
-        out[IO::kKeff + frag_off<KK>(i, j, D)] = OT::from_f(acc[r]);
+        out[IO::kKeff + frag_off<KK>(i, j, D)] = OT::from_f(acc[r] * em);
       }
     }
   }
@@ -458,19 +468,30 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
     *reinterpret_cast<float2*>(partial + tp * D + c0) = float2{s0, s1};
   }
   __syncthreads();
-  float gc0 = 0.f, gc1 = 0.f, off0 = 0.f, off1 = 0.f;
+  // gc: the chunk total; gm: the prefix through token 31 (mid-chunk reference)
+  float gc0 = 0.f, gc1 = 0.f, off0 = 0.f, off1 = 0.f, gm0 = 0.f, gm1 = 0.f;
 #pragma unroll
   for (int p = 0; p < LY::TPARTS; ++p) {
     const float2 v = *reinterpret_cast<const float2*>(partial + p * D + c0);
     if (p < tp) { off0 += v.x; off1 += v.y; }
+    if (p < LY::TPARTS / 2) { gm0 += v.x; gm1 += v.y; }
     gc0 += v.x;
     gc1 += v.y;
   }
   __syncthreads();  // partials are overwritten by Kt^T below
 
   // ---- C: decayed tiles --------------------------------------------------------
+  // The Gram tiles (LDS) are decayed relative to the mid-chunk prefix G_31:
+  // Kt' = K exp(G - G_31), Kh' = K exp(G_31 - G), Qt' = Q exp(G - G_31), whose
+  // products over a channel equal exp(G_i - G_j) K_i K_j as with any other
+  // reference, while each factor stays within exp(+-(half a chunk of gates)).
+  // The state-side pieces keep the chunk-start reference, where every factor
+  // is at most 1: Kt = K exp(G) (Kt^T, for Keff), Qt = Q exp(G) (workspace),
+  // Kend = K exp(G_C - G) (workspace).
   {
     const float eC0 = __builtin_amdgcn_exp2f(gc0), eC1 = __builtin_amdgcn_exp2f(gc1);
+    const float eM0 = __builtin_amdgcn_exp2f(gm0), eM1 = __builtin_amdgcn_exp2f(gm1);
+    const float eCM0 = __builtin_amdgcn_exp2f(gc0 - gm0), eCM1 = __builtin_amdgcn_exp2f(gc1 - gm1);
     uint32_t ktT0[TPP / 2], ktT1[TPP / 2], ke0[TPP / 2], ke1[TPP / 2];
 #pragma unroll
     for (int i = 0; i < TPP; i += 2) {
@@ -478,17 +499,20 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int r = r0 + i + u;
-        const float Ga = G0[i + u] + off0, Gb = G1[i + u] + off1;
+        const float Ga = G0[i + u] + off0 - gm0, Gb = G1[i + u] + off1 - gm1;
         const float e0 = __builtin_amdgcn_exp2f(Ga), e1 = __builtin_amdgcn_exp2f(Gb);
         const float i0 = __builtin_amdgcn_exp2f(-Ga), i1 = __builtin_amdgcn_exp2f(-Gb);
         const float k0 = bf_lo(in.k[i + u]), k1 = bf_hi(in.k[i + u]);
         const float q0 = bf_lo(in.q[i + u]), q1 = bf_hi(in.q[i + u]);
-        const float kh0 = k0 * i0, kh1 = k1 * i1;
-        kt2[u] = pack_bf16x2(k0 * e0, k1 * e1);
-        ke2[u] = pack_bf16x2(kh0 * eC0, kh1 * eC1);
-        *reinterpret_cast<uint32_t*>(Kt + r * LDK + c0) = kt2[u];
+        const float kt0 = k0 * e0, kt1 = k1 * e1, kh0 = k0 * i0, kh1 = k1 * i1;
+        const float qt0 = q0 * e0, qt1 = q1 * e1;
+        kt2[u] = pack_bf16x2(kt0 * eM0, kt1 * eM1);
+        ke2[u] = pack_bf16x2(kh0 * eCM0, kh1 * eCM1);
+        *reinterpret_cast<uint32_t*>(Kt + r * LDK + c0) = pack_bf16x2(kt0, kt1);
         *reinterpret_cast<uint32_t*>(Kh + r * LDK + c0) = pack_bf16x2(kh0, kh1);
-        *reinterpret_cast<uint32_t*>(Qt + r * LDK + c0) = pack_bf16x2(q0 * e0, q1 * e1);
+        *reinterpret_cast<uint32_t*>(Qt + r * LDK + c0) = pack_bf16x2(qt0, qt1);
+        *reinterpret_cast<uint32_t*>(at32(out, IO::kQt + frag_off<32>(r, c0, D))) =
+            pack_bf16x2(qt0 * eM0, qt1 * eM1);
       }
       ktT0[i / 2] = lo_halves(kt2[0], kt2[1]);
       ktT1[i / 2] = hi_halves(kt2[0], kt2[1]);
@@ -517,11 +541,12 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
 
   // ---- D: Gram matrices, formed transposed (M = key token j, N = token i) ---
   // so that a lane holds 4 consecutive columns j of one row i.  Waves 0,1:
-  // A = Kt Kh^T -> L = diag(beta) strictLower(A) (fp32, LDS); waves 2,3:
-  // Aq = lowerIncl(Qt Kh^T) (bf16, to the workspace, as are their Qt
-  // fragments).  Each wave takes row blocks {0,3} or {1,2} (5 lower tiles;
-  // the upper tiles of Aq inside fragments the scan reads are written as
-  // zeros).
+  // A = Kt' Kh'^T -> L = diag(beta) strictLower(A) (fp32, LDS); waves 2,3:
+  // Aq = lowerIncl(Qt' Kh'^T) (bf16, to the workspace).  Each wave takes row
+  // blocks {0,3} or {1,2} (5 lower tiles; the upper tiles of Aq inside
+  // fragments the scan reads are written as zeros).  Products right of the
+  // diagonal are computed and discarded by selects: with strong decay they
+  // may overflow, which the selects keep out of the results.
   {
     const int gram = wv >> 1;
     const uint16_t* Bop = gram == 0 ? Kt : Qt;
@@ -533,11 +558,6 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
       Frag<uint16_t> bf[NKD];
 #pragma unroll
       for (int k = 0; k < NKD; ++k) bf[k] = frag<uint16_t>(Bop, LDK, 16 * nt, 32 * k, lane);
-      if (gram == 1) {  // Qt rows 16nt.. are one fragment row of the workspace copy
-#pragma unroll
-        for (int k = 0; k < NKD; ++k)
-          *reinterpret_cast<u16x8*>(at32(out, IO::kQt + (uint32_t)((nt * NKD + k) * 64 + lane) * 8u)) = bf[k].v;
-      }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {  // column block of j
         acc[pass][mt] = zero4();

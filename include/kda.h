@@ -176,9 +176,13 @@ size_t kda_prefill_workspace_min_bytes(const kda_pool* pool, int32_t num_seqs, i
  *
  * Numerics: bf16 inputs run the chunk products on bf16 MFMA with fp32
  * accumulation and an fp32 carried state; fp32 inputs run them in fp32.
- * Domain: the chunk form factors the decay as exp(+G) and exp(-G) with G the
- * within-chunk prefix sum of g; it needs |G| < 80 in every channel of every
- * chunk (mean log alpha > -1.25 per token).
+ * Domain: with G the within-chunk prefix sum of g (g <= 0), the chunk form
+ * uses exp(G) and exp(G_C - G) (at most 1) for the state-side operands and
+ * exp(+-(G - G_31)) for the intra-chunk Gram products (G_31: the prefix
+ * through the chunk's 32nd token).  It needs |G_i - G_31| < 87 in every
+ * channel, token i and chunk, so that every factor is a normal fp32 number:
+ * any gate sum over half a chunk above -87 (a mean log alpha above -2.7 per
+ * token suffices).  Past it, results lose accuracy or become non-finite.
  * Tuning: the environment variable KDA_SCAN_SLAB=1 or 2 forces 16- or
  * 32-column state slabs in the scan (by default 32 when that still gives every
  * CU a workgroup); results are bit-identical either way.

@@ -82,6 +82,103 @@ def test_small_cases(dtype, D, H, cu):
             assert np.all(pb.states(s) == 0)
 
 
+def _f64(x, dtype):
+    """Stored input values (bf16 bit patterns or fp32) as float64."""
+    if dtype == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def _const(x, dtype, value):
+    """An input array of the generator's shape and dtype holding `value`."""
+    if dtype == "bf16":
+        bits = np.float32(value).view(np.uint32) >> 16  # value is exact in bf16
+        return np.full(x.shape, bits, np.uint16)
+    return np.full(x.shape, value, x.dtype)
+
+
+@pytest.mark.parametrize("dtype,g_lo,g_hi", [
+    ("bf16", -1.2, 0.0), ("f32", -1.2, 0.0),   # strong, mixed decay
+    ("bf16", -2.7, -2.6), ("f32", -2.7, -2.6),  # edge: ~86 of log-decay per half chunk
+])
+def test_strong_decay(dtype, g_lo, g_hi):
+    """Strong per-channel decay.  With g near -2.7 every channel's log decay over
+    a chunk is about -173, far past the fp32 range of exp; the chunk form keeps
+    each factor within one half chunk of the middle (|G - G_31| <= ~86) and
+    matches the oracle, o and every checkpoint and final state, with a resumed
+    second sequence and a ragged tail."""
+    H, D = 2, 128
+    cu = [0, 1000, 1700]
+    d = G.kda_tokens(4242, H, D, 0, cu[-1], dtype, g_lo=g_lo, g_hi=g_hi)
+    s0 = (np.random.default_rng(7).standard_normal((H, D, D)) / np.sqrt(D)).astype(np.float32)
+    pb = PoolBuf(6, H, D)
+    pb.set_states(5, s0)
+    ck = dict(ckpt_cu=[0, 1, 2], ckpt_pos=[512, 1536], ckpt_page=[2, 3])
+    o = prefill(pb, inputs_to_dev(d, dtype), cu, dtype, start_pos=[0, 1024],
+                state_in_page=[-1, 5], state_out_page=[0, 1], **ck)
+    s_in = np.zeros((2, H, D, D))
+    s_in[1] = s0
+    ref = _oracle_prefill(d, cu, start_pos=[0, 1024], s0=s_in, **{k: ck[k] for k in ("ckpt_cu", "ckpt_pos")})
+    got = o.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = max_rel_blocks(got, ref["o"], cu, H)
+    for m, p in enumerate(ck["ckpt_page"]):
+        err = max(err, max(rel_fro(pb.states(p)[h], ref["ckpts"][m, h]) for h in range(H)))
+    for s_ in range(2):
+        err = max(err, max(rel_fro(pb.states(s_)[h], ref["s_final"][s_, h]) for h in range(H)))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_identity_beta0_alpha1(dtype):
+    """beta = 0 and alpha = 1 (g = 0): S_t = S_{t-1}.  The entering state comes
+    back bit for bit in every checkpoint and in the final state, and
+    o_t = S0^T q_t matches the oracle."""
+    H, D = 2, 128
+    T = 700
+    d = G.kda_tokens(99, H, D, 0, T, dtype)
+    d["beta"] = _const(d["beta"], dtype, 0.0)
+    d["g"] = _const(d["g"], dtype, 0.0)
+    s0 = (np.random.default_rng(11).standard_normal((H, D, D)) / np.sqrt(D)).astype(np.float32)
+    pb = PoolBuf(4, H, D)
+    pb.set_states(3, s0)
+    o = prefill(pb, inputs_to_dev(d, dtype), [0, T], dtype, start_pos=[512], state_in_page=[3],
+                state_out_page=[0], ckpt_cu=[0, 1], ckpt_pos=[1024], ckpt_page=[1])
+    assert np.array_equal(pb.states(0), s0.astype(np.float64))
+    assert np.array_equal(pb.states(1), s0.astype(np.float64))
+    ref = _oracle_prefill(d, [0, T], start_pos=[512], s0=s0[None].astype(np.float64))
+    err = max_rel_blocks(o.double().cpu().numpy(), ref["o"], [0, T], H)
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_write_beta1_unit_key(dtype):
+    """beta = 1 with unit keys: the delta rule overwrites the value stored under
+    the key, S_t^T k_t = v_t (up to ||k_t||^2 - 1, the rounding of the stored
+    keys).  Checked on the final state against the last token, and against
+    the oracle."""
+    H, D = 2, 128
+    T = 333
+    d = G.kda_tokens(2718, H, D, 0, T, dtype)
+    d["beta"] = _const(d["beta"], dtype, 1.0)
+    pb = PoolBuf(2, H, D)
+    o = prefill(pb, inputs_to_dev(d, dtype), [0, T], dtype, state_out_page=[0])
+    k_last, v_last = _f64(d["k"][T - 1], dtype), _f64(d["v"][T - 1], dtype)
+    S = pb.states(0)
+    for h in range(H):
+        kn2 = float(k_last[h] @ k_last[h])
+        got = S[h].T @ k_last[h]
+        # S'^T k + ||k||^2 (v - S'^T k) = v + (||k||^2 - 1)(v - S'^T k)
+        # plus the state's own error, at most TOL * ||S||_F (checked below)
+        bound = (2 * abs(kn2 - 1.0) * (np.linalg.norm(v_last[h]) + np.linalg.norm(got))
+                 + TOL[dtype] * np.linalg.norm(S[h]))
+        assert np.linalg.norm(got - v_last[h]) <= bound, (h, np.linalg.norm(got - v_last[h]), bound)
+    ref = _oracle_prefill(d, [0, T])
+    err = max(rel_fro(S[h], ref["s_final"][0, h]) for h in range(H))
+    err = max(err, max_rel_blocks(o.double().cpu().numpy(), ref["o"], [0, T], H))
+    assert err <= TOL[dtype], err
+
+
 @pytest.mark.parametrize("page_bytes", [2 << 20, (2 << 20) + 4096])
 def test_prefill_8k_full(page_bytes):
     """H=32, d=128, T=8192, bf16 inputs, fp32 state, checkpoints {2560, 6144, 8192}
