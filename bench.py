@@ -39,10 +39,6 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 # plus 64 KiB per (checkpoint, head) stored.
 PREFILL_BYTES_PER_TOKEN_HEAD = 1282
 PREFILL_FLOPS_PER_TOKEN_HEAD = 131072
-# split of the per-(token, head) bytes between the two prefill kernels:
-#   prep reads q, k, g, beta; scan reads v, writes o and the state pages
-PREP_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 2
-SCAN_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2
 
 
 # HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs over this
@@ -52,13 +48,13 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_prefill8k_decode25
 KERNEL_SOURCES = {"kda_prefill_prep": "kda_prefill.hip", "kda_prefill_scan": "kda_prefill.hip",
                   "kda_decode_step": "kda_decode.hip", "kda_page_copy": "kda_copy.hip",
                   "kda_ckpt_quant": "kda_ckpt_int8.hip", "kda_ckpt_dequant": "kda_ckpt_int8.hip",
-                  "kda_short_conv": "kda_conv.hip"}
+                  "kda_short_conv": "kda_conv.hip", "kda_short_conv_update": "kda_conv.hip"}
 # device kernel symbol -> library launch name
 KERNEL_SYMBOLS = {"prep2_kernel": "kda_prefill_prep", "prep_kernel": "kda_prefill_prep",
                   "scan_kernel": "kda_prefill_scan", "decode_kernel": "kda_decode_step",
                   "copy_kernel": "kda_page_copy", "meta_fill_kernel": "kda_meta_fill",
                   "quant_kernel": "kda_ckpt_quant", "dequant_kernel": "kda_ckpt_dequant",
-                  "conv_kernel": "kda_short_conv"}
+                  "conv_kernel": "kda_short_conv", "conv_update_kernel": "kda_short_conv_update"}
 
 
 def log(*a):
@@ -329,7 +325,11 @@ def bench_long(K, G, steps=3, warmup=1):
             "inputs": "drawn on the device (seeded torch generator, the generator's distributions)"}
 
 
-def bench_decode(K, G, steps, warmup, n_inputs=32):
+def bench_decode(K, G, steps=1000, warmup=10):
+    """Decode workload: 256 requests x 32 heads, fp32 states in a 512-page pool
+    reached through a random page table, one launch per step, `steps`
+    consecutive steps each with its own token inputs (drawn on the device with
+    the generator's distributions, all resident before timing)."""
     import torch
     w = G.DECODE_256
     pt = torch.from_numpy(G.decode_page_table(w)).cuda()
@@ -340,8 +340,8 @@ def bench_decode(K, G, steps, warmup, n_inputs=32):
     for r, p in enumerate(pt.cpu().numpy()):
         pool_buf[p * words:p * words + sb] = torch.from_numpy(s0[r].reshape(-1)).cuda().view(torch.int32)
     pool = K.make_pool(pool_buf, w.page_bytes, w.pool_pages, w.H, w.D)
-    d = G.kda_tokens(w.seed, w.H, w.D, 0, n_inputs * w.n_req, w.dtype)
-    di = {k: to_dev(v, w.dtype) for k, v in d.items()}
+    n_inputs = steps + warmup
+    di = device_tokens(n_inputs * w.n_req, w.H, w.D, w.seed, w.dtype)
     o = torch.empty((w.n_req, w.H, w.D), dtype=torch.bfloat16, device="cuda")
     it = [0]
 
@@ -358,10 +358,13 @@ def bench_decode(K, G, steps, warmup, n_inputs=32):
     io_bytes = w.n_req * w.H * (4 * w.D * 2 + 2 + w.D * 2)     # q,k,v,g,beta in; o out
     per_step = state_bytes + io_bytes
     avg = kt["kda_decode_step"]["avg_ms"] / 1e3
+    del di
     return {
         "workload": w.name, "steps": steps, "distinct_input_sets": n_inputs,
+        "inputs": "drawn on the device (seeded torch generator, the generator's distributions)",
         "ms_per_step": 1e3 * dev_s / steps, "bytes_per_step": per_step,
         "gbps": per_step / (dev_s / steps) / 1e9,
+        "frac_hbm_step": per_step / (dev_s / steps) / 1e9 / HBM_PEAK_GBS,
         "kernel_avg_ms": 1e3 * avg, "kernel_gbps": per_step / avg / 1e9,
         "frac_hbm": per_step / avg / 1e9 / HBM_PEAK_GBS,
         "tokens_per_s": w.n_req * steps / dev_s,
@@ -471,76 +474,155 @@ def bench_conv(K, G, steps=20, warmup=5, T=8192, C=3 * 32 * 128, W=4):
             "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_conv_decode(K, G, steps=200, warmup=10, n=256, C=3 * 32 * 128, W=4):
+    """The decode-step conv update: 256 requests x one token over the fused
+    q|k|v channels (12,288, bf16), width 4, each request reading its window
+    page and writing the next one (pages alternate between steps).  Timed
+    through kda_short_conv_update (device page tables) and, for comparison,
+    through kda_short_conv with 256 one-token sequences (host tables)."""
+    import torch
+    x = to_dev(G.conv_inputs(12, n, C, "bf16"), "bf16")
+    wt = torch.from_numpy(G.conv_weights(12, C, W)).cuda()
+    y = torch.empty(n, C, dtype=torch.bfloat16, device="cuda")
+    win = (W - 1) * C * 2
+    pb = (win + 255) // 256 * 256
+    cbuf = torch.zeros(2 * n * pb, dtype=torch.uint8, device="cuda")
+    cpool = K.make_conv_pool(cbuf, pb, 2 * n, C, W, K.KDA_BF16)
+    wsb = torch.empty(K.kda_conv_workspace_bytes(n, 0), dtype=torch.uint8, device="cuda")
+    cu = np.arange(n + 1, dtype=np.int64)
+    pages = [list(range(n)), list(range(n, 2 * n))]
+    dpages = [torch.tensor(p, dtype=torch.int32, device="cuda") for p in pages]
+    moved = n * (2 * C * 2 + 2 * win) + C * W * 4  # x in, y out, window in and out, taps
+    it = [0]
+
+    def step_update():
+        t = it[0]
+        it[0] += 1
+        K.kda_short_conv_update(cpool, x, wt, y, dpages[t % 2], dpages[(t + 1) % 2])
+
+    def step_tables():
+        t = it[0]
+        it[0] += 1
+        K.kda_short_conv(cpool, x, wt, y, cu, start_pos=[100 + t] * n, state_in_page=pages[t % 2],
+                         state_out_page=pages[(t + 1) % 2], workspace=wsb)
+    out = {"requests": n, "channels": C, "width": W, "tokens_per_request": 1, "bytes_per_call": moved}
+    for name, fn, kern in (("update", step_update, "kda_short_conv_update"),
+                           ("short_conv_1tok_seqs", step_tables, "kda_short_conv")):
+        dev_s, _ = timed(fn, steps, warmup)
+        kt = kernel_times(K, fn, steps)
+        avg = kt[kern]["avg_ms"] / 1e3
+        out[name] = {"ms_per_call": 1e3 * dev_s / steps, "kernel_avg_ms": 1e3 * avg,
+                     "kernel_gbps": moved / avg / 1e9, "frac_hbm": moved / avg / 1e9 / HBM_PEAK_GBS,
+                     "frac_hbm_call": moved / (dev_s / steps) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
+def index_workload(G, pb=6144):
+    """Token streams of the prefix-index workload: a 2^20-token session, 64
+    agentic sessions of 32,768 tokens sharing a 4096-token system prompt, and
+    one request per session diverging at a random point (plus one diverging
+    from the long session at 900,000 tokens)."""
+    long_t = G.token_ids(21, 1 << 20)
+    system = G.token_ids(22, 4096)
+    sessions = [np.concatenate([system, G.token_ids(23, 32768 - 4096, seq_id=s)]) for s in range(64)]
+    rng = np.random.default_rng(5)
+    cuts = rng.integers(4096, 32768, 64)
+    reqs = [np.concatenate([sessions[i][:cuts[i]], G.token_ids(25, 500, seq_id=i)]) for i in range(64)]
+    req_long = np.concatenate([long_t[:900_000], G.token_ids(24, 1000)])
+    # whole 6144-token pages match, then the deepest 4096-multiple checkpoint
+    expect = [int(c) // pb * pb // 4096 * 4096 for c in cuts]
+    return dict(long_t=long_t, sessions=sessions, reqs=reqs, req_long=req_long, expect=expect)
+
+
 def bench_index(K, G, reps=100):
     """Host prefix index (no GPU): a 2^20-token session in 6144-token pages with
     a checkpoint every 6144 tokens in 2 KDA groups, plus 64 agentic sessions of
     32,768 tokens sharing a 4096-token system prompt (a checkpoint every 4096
     tokens).  Timed: lookup + pin + release of the long session diverging at
-    900,000 tokens, and of each short session diverging at a random point; the
-    oracle (token-prefix comparison, no hashing) on a sample of the short ones."""
-    from oracle.prefix_index import PrefixIndexModel
+    900,000 tokens, and of each short session diverging at a random point; every
+    boundary is checked against the closed form of the workload."""
     hb, pb, groups = 512, 6144, 2
+    wl = index_workload(G, pb)
     idx = K.kda_index_create(hb, pb, groups, namespace_seed=1)
-    model = PrefixIndexModel(hb, pb, groups)
     ck = [1_000_000]
 
-    def add(t, every, page0, to_model):
+    def add(t, every, page0):
         npg = -(-len(t) // pb)
         K.kda_index_register_pages(idx, t, list(range(page0, page0 + npg)))
-        if to_model:
-            model.register_pages(t, list(range(page0, page0 + npg)), 0)
         for b in range(every, len(t) + 1, every):
             for g in range(groups):
                 ck[0] += 1
                 K.kda_index_register_ckpt(idx, t, b, g, ck[0], durable=True)
-                if to_model:
-                    model.register_ckpt(t, b, g, ck[0], True, 0)
         return page0 + npg
 
-    long_t = G.token_ids(21, 1 << 20)
-    page = add(long_t, pb, 0, False)
-    system = G.token_ids(22, 4096)
-    sessions = []
-    for s in range(64):
-        t = np.concatenate([system, G.token_ids(23, 32768 - 4096, seq_id=s)])
-        page = add(t, 4096, page, s < 8)
-        sessions.append(t)
+    page = add(wl["long_t"], pb, 0)
+    for t in wl["sessions"]:
+        page = add(t, 4096, page)
     K.kda_index_mark_ready(idx, 0)
-    model.mark_ready(0)
-    rng = np.random.default_rng(5)
-    req_long = np.concatenate([long_t[:900_000], G.token_ids(24, 1000)])
-    cuts = rng.integers(4096, 32768, 64)
-    reqs = [np.concatenate([sessions[i][:cuts[i]], G.token_ids(25, 500, seq_id=i)]) for i in range(64)]
 
     def one(r):
         h = K.kda_index_lookup(idx, r, pin=True)
         if h["pin_handle"]:
             K.kda_index_release(idx, h["pin_handle"])
         return h
-    hl = one(req_long)
+    hl = one(wl["req_long"])
+    assert hl["boundary"] == 900_000 // pb * pb
+    for r, e in zip(wl["reqs"], wl["expect"]):
+        assert one(r)["boundary"] == e
     t0 = time.perf_counter()
     for _ in range(reps):
-        one(req_long)
+        one(wl["req_long"])
     t_long = (time.perf_counter() - t0) / reps
     t0 = time.perf_counter()
     for _ in range(reps // 10):
-        for r in reqs:
+        for r in wl["reqs"]:
             one(r)
-    t_short = (time.perf_counter() - t0) / (reps // 10 * len(reqs))
-    t0 = time.perf_counter()
-    for i, r in enumerate(reqs[:8]):
-        b = model.lookup(r)["boundary"]
-        # whole 6144-token pages match, then the deepest 4096-multiple checkpoint
-        assert b == K.kda_index_lookup(idx, r)["boundary"] == cuts[i] // pb * pb // 4096 * 4096
-    t_oracle = (time.perf_counter() - t0) / 8
-    assert hl["boundary"] == 900_000 // pb * pb
-    n_long = len(req_long)
+    t_short = (time.perf_counter() - t0) / (reps // 10 * len(wl["reqs"]))
+    n_long = len(wl["req_long"])
+    stats = K.kda_index_stats(idx)[:2]
+    K.kda_index_destroy(idx)
     return {"long_1m": {"tokens": n_long, "boundary": hl["boundary"], "pages": len(hl["pages"]),
                         "ms_per_lookup": 1e3 * t_long,
                         "hashed_gb_per_s": n_long * 4 / t_long / 1e9},
             "sessions_32k": {"us_per_lookup": 1e6 * t_short, "lookups_per_s": 1.0 / t_short},
-            "oracle_32k_ms_per_lookup": 1e3 * t_oracle,
-            "entries": K.kda_index_stats(idx)[:2]}
+            "entries": stats}
+
+
+def cpu_index_oracle(G, n=8):
+    """The prefix-index oracle (token-prefix comparison, no hashing) on the first
+    n sessions of the index workload: registration excluded, lookups timed, each
+    boundary checked against the workload's closed form."""
+    from oracle.prefix_index import PrefixIndexModel
+    hb, pb, groups = 512, 6144, 2
+    wl = index_workload(G, pb)
+    model = PrefixIndexModel(hb, pb, groups)
+    ck, page = 1_000_000, 0
+    for t in wl["sessions"][:n]:
+        npg = -(-len(t) // pb)
+        model.register_pages(t, list(range(page, page + npg)), 0)
+        page += npg
+        for b in range(4096, len(t) + 1, 4096):
+            for g in range(groups):
+                ck += 1
+                model.register_ckpt(t, b, g, ck, True, 0)
+    model.mark_ready(0)
+    t0 = time.perf_counter()
+    for r, e in zip(wl["reqs"][:n], wl["expect"][:n]):
+        assert model.lookup(r)["boundary"] == e
+    el = (time.perf_counter() - t0) / n
+    return {"value": 1.0 / el, "unit": "lookups/s", "ms_per_lookup": 1e3 * el, "cores": 1,
+            "kind": "oracle", "sample": f"{n} of the 64 agentic 32K-token sessions"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(G, w, d):
@@ -554,6 +636,7 @@ def cpu_baseline(G, w, d):
                ckpt_pos=list(w.ckpts), threads=threads)
     el = time.perf_counter() - t0
     return {"value": w.T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"whole workload: {w.T} tokens x {w.H} heads, fp64 token loop, "
                       f"{el:.2f} s, OpenMP over heads"}
 
@@ -601,17 +684,23 @@ def main():
     tok_s = w.T * args.steps / dev_s
     log(f"prefill: {ms_step:.3f} ms/step, {tok_s / 1e6:.2f} M tokens/s; kernels {kt}")
 
-    # roofline of the dominant kernel (HBM-bound, algorithmic bytes per launch)
+    # Roofline of the call (the whole hot path: prep and scan of every window,
+    # metadata, checkpoint and final-state stores), counted as the method's
+    # algorithmic work: 1282 B and 131072 flop per (token, head), plus 64 KiB
+    # per (checkpoint, head) and per (final state, head); over the step time
+    # measured with HIP events on the stream the library launches on.
     th = w.T * w.H
     ck_bytes = len(w.ckpts) * w.H * w.D * w.D * 4 + w.H * w.D * w.D * 4  # checkpoints + final state
-    alg = {"kda_prefill_prep": th * PREP_BYTES_PER_TOKEN_HEAD,
-           "kda_prefill_scan": th * SCAN_BYTES_PER_TOKEN_HEAD + ck_bytes}
-    dom = max(alg, key=lambda n: kt[n]["avg_ms"])
-    dom_s = kt[dom]["avg_ms"] / 1e3
-    achieved = alg[dom] / dom_s / 1e9
     call_bytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + ck_bytes
     call_flops = th * PREFILL_FLOPS_PER_TOKEN_HEAD
     step_s = dev_s / args.steps
+    reps = max(args.steps, 5)
+    per_call = {n: v["launches"] / reps for n, v in kt.items()}
+    traffic = None
+    tr = {n: recorded_traffic(n) for n in ("kda_prefill_prep", "kda_prefill_scan")}
+    if all(v is not None for v in tr.values()):
+        traffic = sum(tr[n] * per_call.get(n, 0) for n in tr)
+    achieved = call_bytes / step_s / 1e9
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
@@ -620,21 +709,23 @@ def main():
         "config": {"workload": w.name, "H": w.H, "d": w.D, "T": w.T, "chunk": 64,
                    "checkpoints": list(w.ckpts), "page_bytes": w.page_bytes,
                    "state_dtype": "f32", "io_dtype": "bf16"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic(dom),
-                     "algorithmic_bytes_per_launch": alg[dom],
-                     "avg_launch_ms": 1e3 * dom_s},
-        "prefill_step": {"algorithmic_bytes": call_bytes, "algorithmic_flops": call_flops,
-                         "frac_hbm": call_bytes / step_s / 1e9 / HBM_PEAK_GBS,
-                         "frac_mfma_bf16": call_flops / step_s / 1e12 / BF16_PEAK_TFLOPS,
-                         "wall_s": wall_s},
-        "kernels": kt,
+        "roofline": {"bound": "hbm", "kernel": "kda_prefill_chunked (whole call: prep + scan per window)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_call": call_bytes, "step_ms": 1e3 * step_s,
+                     "frac_mfma_bf16": call_flops / step_s / 1e12 / BF16_PEAK_TFLOPS,
+                     "frac_attainable": max(call_flops / (BF16_PEAK_TFLOPS * 1e12),
+                                            call_bytes / (HBM_PEAK_GBS * 1e9)) / step_s,
+                     "algorithmic_flops_per_call": call_flops},
+        "kernels_diagnostic": {n: {"launches_per_call": per_call[n], "avg_ms": v["avg_ms"],
+                                   "ms_per_call": v["avg_ms"] * per_call[n]} for n, v in kt.items()},
+        "prefill_wall_s": wall_s,
         "prefill_graph": graph,
     }
     if not args.only_prefill:
         log("decode: 256 requests x 32 heads")
-        out["decode"] = bench_decode(K, G, steps=200, warmup=10)
+        out["decode"] = bench_decode(K, G)
+        torch.cuda.empty_cache()
         log(f"decode: {out['decode']}")
         out["checkpoint_copy"] = bench_copy(K, steps=20, warmup=3)
         log(f"copy: {out['checkpoint_copy']}")
@@ -644,6 +735,8 @@ def main():
         log(f"verify: {out['verify']}")
         out["short_conv"] = bench_conv(K, G)
         log(f"conv: {out['short_conv']}")
+        out["short_conv_decode"] = bench_conv_decode(K, G)
+        log(f"conv decode: {out['short_conv_decode']}")
         out["prefix_index"] = bench_index(K, G)
         log(f"index: {out['prefix_index']}")
     if not args.only_prefill and not args.only_core:
@@ -658,6 +751,8 @@ def main():
     if not args.no_cpu:
         log("cpu baseline: oracle")
         out["cpu_baseline"] = cpu_baseline(G, w, d)
+        if not args.only_prefill:
+            out["cpu_baseline"]["prefix_index"] = cpu_index_oracle(G)
     print(json.dumps(out), flush=True)
 
 

@@ -39,7 +39,7 @@ EXPORTS = ("kda_version", "kda_last_error", "kda_pool_check", "kda_state_offset"
            "kda_prefill_chunked_noalloc", "kda_decode_step", "kda_decode_verify",
            "kda_checkpoint_write", "kda_checkpoint_restore", "kda_ckpt_int8_head_bytes",
            "kda_checkpoint_write_int8", "kda_checkpoint_restore_int8",
-           "kda_conv_workspace_bytes", "kda_short_conv", "kda_profile_enable", "kda_profile_read",
+           "kda_conv_workspace_bytes", "kda_short_conv", "kda_short_conv_update", "kda_profile_enable", "kda_profile_read",
            "kda_xxh64", "kda_chain_hashes", "kda_ckpt_plan", "kda_index_create",
            "kda_index_destroy", "kda_index_register_pages", "kda_index_register_ckpt",
            "kda_index_mark_ready", "kda_index_lookup", "kda_index_release", "kda_index_evict_page",
@@ -107,6 +107,8 @@ _sig = {
     "kda_conv_workspace_bytes": (_i64, [_i32, _i32]),
     "kda_short_conv": (ctypes.c_int, [ctypes.POINTER(kda_conv_pool), _P, _P, _P, ctypes.c_int, _i32,
                                       _P, _P, _P, _P, _P, _P, _P, _i32, _P, _sz, _P]),
+    "kda_short_conv_update": (ctypes.c_int, [ctypes.POINTER(kda_conv_pool), _P, _P, _P, ctypes.c_int,
+                                             _i32, _P, _P, _P]),
     "kda_xxh64": (ctypes.c_uint64, [_P, _i64, ctypes.c_uint64]),
     "kda_chain_hashes": (_i64, [_P, _i64, _i32, ctypes.c_uint64, _P, _i64]),
     "kda_ckpt_plan": (_i64, [_i64, _i64, _i32]),
@@ -389,6 +391,17 @@ def kda_short_conv(cpool, x, w, y, cu_seqlens, *, start_pos=None, state_in_page=
     st = _lib.kda_short_conv(ctypes.byref(cpool), _dptr(x), _dptr(w), _dptr(y), outd, ns, cu.ptr,
                              sp.ptr, si.ptr, so.ptr, ccu.ptr, cpos.ptr, cpg.ptr, hash_block,
                              _dptr(workspace), workspace_bytes, _stream(stream))
+    _check(st)
+
+
+def kda_short_conv_update(cpool, x, w, y, page_in, page_out, *, n=None, out_dtype=None,
+                          stream=None):
+    """One token per request: x, y [n, C] device tensors, w [C, W] fp32 device
+    tensor, page_in / page_out int32 device tensors [n]."""
+    n = int(page_in.numel()) if n is None else n
+    outd = _dtype_code(y) if out_dtype is None else out_dtype
+    st = _lib.kda_short_conv_update(ctypes.byref(cpool), _dptr(x), _dptr(w), _dptr(y), outd, n,
+                                    _dptr(page_in), _dptr(page_out), _stream(stream))
     _check(st)
 
 

@@ -644,6 +644,49 @@ kda_status kda_short_conv(const kda_conv_pool* cpool, const void* x, const float
   return ok();
 }
 
+kda_status kda_short_conv_update(const kda_conv_pool* cpool, const void* x, const float* w, void* y,
+                                 kda_dtype out_dtype, int32_t n, const int32_t* page_in,
+                                 const int32_t* page_out, void* stream) {
+  const char* what = "kda_short_conv_update";
+  kda_status s = check_conv_pool(cpool);
+  if (s != KDA_OK) return s;
+  if (!valid_dtype(out_dtype)) return fail(KDA_ERR_DTYPE, "%s: unknown out dtype %d", what, (int)out_dtype);
+  if (n < 0) return fail(KDA_ERR_SHAPE, "%s: n < 0", what);
+  if (n == 0) return ok();
+  if (!x || !y || !w || !page_in || !page_out)
+    return fail(KDA_ERR_NULL, "%s: x, w, y, page_in and page_out must be non-NULL", what);
+  for (const void* p : {x, static_cast<const void*>(y), static_cast<const void*>(w)})
+    if (!aligned(p, 16)) return fail(KDA_ERR_SHAPE, "%s: x, y, w must be 16-byte aligned", what);
+  if (x == y) return fail(KDA_ERR_SHAPE, "%s: y may not alias x", what);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const char* val = std::getenv("KDA_VALIDATE");
+  if (val && val[0] == '1') {
+    std::vector<int32_t> pin(n), pout(n);
+    hipError_t e = hipMemcpyAsync(pin.data(), page_in, (size_t)n * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(pout.data(), page_out, (size_t)n * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "page table read-back");
+    std::unordered_set<int32_t> outs;
+    for (int32_t r = 0; r < n; ++r) {
+      if (pin[r] < 0 || pin[r] >= cpool->num_pages)
+        return fail(KDA_ERR_PAGE_RANGE, "%s: request %d: page_in %d out of range", what, r, pin[r]);
+      if (pout[r] < 0 || pout[r] >= cpool->num_pages)
+        return fail(KDA_ERR_PAGE_RANGE, "%s: request %d: page_out %d out of range", what, r, pout[r]);
+      if (!outs.insert(pout[r]).second) return fail(KDA_ERR_PAGE_ALIAS, "%s: page_out %d repeats", what, pout[r]);
+    }
+    for (int32_t r = 0; r < n; ++r)
+      if (outs.count(pin[r]) && pout[r] != pin[r])
+        return fail(KDA_ERR_PAGE_ALIAS, "%s: page_in[%d] = %d is another request's output", what, r, pin[r]);
+  }
+  ConvUpdateArgs a{x, w, y, page_in, page_out, static_cast<uint8_t*>(cpool->base), cpool->page_bytes,
+                   cpool->num_pages, n, cpool->channels, cpool->width, cpool->dtype == KDA_BF16,
+                   out_dtype == KDA_BF16};
+  Launch L("kda_short_conv_update", st);
+  hipError_t e = launch_conv_update(a, st);
+  if (e != hipSuccess) return hip_fail(e, "conv update launch");
+  return ok();
+}
+
 // ---- int8 compressed checkpoints ----------------------------------------------
 
 int64_t kda_ckpt_int8_head_bytes(int32_t d_k, int32_t d_v) {

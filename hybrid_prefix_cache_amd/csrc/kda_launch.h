@@ -198,8 +198,27 @@ kda_status prefill_impl(const kda_pool* pool, const void* q, const void* k, cons
                         int32_t hash_block, void* workspace, size_t workspace_bytes,
                         kda_status (*scratch)(void**), void* stream);
 
+// One kda_short_conv_update call: request r's window page_in[r] and token
+// row r of x -> y row r and the next window in page_out[r].
+struct ConvUpdateArgs {
+  const void* x;
+  const float* w;
+  void* y;
+  const int32_t* page_in;   // device [n]
+  const int32_t* page_out;  // device [n]
+  uint8_t* cpool;
+  int64_t cpage_bytes;
+  int32_t num_pages;
+  int32_t n;
+  int32_t C;
+  int32_t W;
+  int32_t in_bf16;
+  int32_t out_bf16;
+};
+
 hipError_t launch_copy(const CopyArgs& a, hipStream_t st);
 hipError_t launch_conv(const ConvArgs& a, int32_t total_chunks, hipStream_t st);
+hipError_t launch_conv_update(const ConvUpdateArgs& a, hipStream_t st);
 hipError_t launch_quant(int D, const QuantArgs& a, hipStream_t st);
 hipError_t launch_dequant(int D, const QuantArgs& a, hipStream_t st);
 

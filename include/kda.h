@@ -370,6 +370,33 @@ kda_status kda_short_conv(const kda_conv_pool* cpool, const void* x, const float
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode-step convolution update: one token for each of n requests.  Request
+ * r reads its window (the W-1 most recent inputs, as kda_short_conv stores
+ * them) from page page_in[r], computes y row r from it and x row r, and
+ * writes the next window (the last W-2 window rows, then x row r) to page
+ * page_out[r].  Same arithmetic as kda_short_conv, so equal inputs give equal
+ * bits (page "KIMI K3 경량 복제에서 본 KDA의 AI 인프라 과제", sections 6.4
+ * and 8.2.3: in decode the convolution state is updated one token at a time
+ * next to the recurrent state).
+ *   x : [n, C] (cpool->dtype, device); w : [C][W] fp32 (device);
+ *   y : [n, C] (out_dtype, device; may not alias x)
+ *   page_in, page_out : [n] int32 DEVICE arrays (no host synchronisation per
+ *   step).  page_out[r] == page_in[r] updates in place.  The caller
+ *   guarantees that the page_out entries are distinct and that no page_out[r]
+ *   equals page_in[r'] for r' != r.  Device-side: a request whose page index
+ *   is outside [0, num_pages) touches no page and gets NaN outputs.  With the
+ *   environment variable KDA_VALIDATE=1 the page tables are copied to the
+ *   host and checked first (this synchronises the stream).  A checkpoint of
+ *   the window at a hash-block boundary is the page_out of the token that
+ *   ends there.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_POOL,
+ * KDA_ERR_PAGE_RANGE / KDA_ERR_PAGE_ALIAS (KDA_VALIDATE=1 only), KDA_ERR_HIP.
+ */
+kda_status kda_short_conv_update(const kda_conv_pool* cpool, const void* x, const float* w, void* y,
+                                 kda_dtype out_dtype, int32_t n, const int32_t* page_in,
+                                 const int32_t* page_out, void* stream);
+
+/*
  * Optional per-kernel timing (tracing aid).  When enabled, every kernel the
  * library launches is bracketed by a pair of HIP events on its own stream;
  * kda_profile_read synchronises those events and returns, per kernel name, the

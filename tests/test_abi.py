@@ -178,6 +178,31 @@ def test_workspace_bound_matches_check():
     assert K.kda_prefill_workspace_min_bytes(p, -1, 0, K.KDA_BF16) == 0
 
 
+def test_conv_update_validation():
+    """kda_short_conv_update rejects bad arguments before touching the device."""
+    cp = K.make_conv_pool(FAKE, 3 * 12288 * 2, 8, 12288, 4, K.KDA_BF16)
+    base = dict(cpool=cp, x=FAKE, w=FAKE, y=FAKE + 4096, page_in=FAKE, page_out=FAKE, n=4,
+                out_dtype=K.KDA_BF16, stream=0)
+    for kw, status in ((dict(x=0), K.KDA_ERR_NULL), (dict(page_out=0), K.KDA_ERR_NULL),
+                       (dict(y=FAKE + 8), K.KDA_ERR_SHAPE), (dict(y=FAKE), K.KDA_ERR_SHAPE),
+                       (dict(n=-1), K.KDA_ERR_SHAPE), (dict(out_dtype=4), K.KDA_ERR_DTYPE)):
+        a = dict(base)
+        a.update(kw)
+        c = a.pop("cpool")
+        with pytest.raises(K.KdaError) as e:
+            K.kda_short_conv_update(c, a.pop("x"), a.pop("w"), a.pop("y"), a.pop("page_in"),
+                                    a.pop("page_out"), **a)
+        assert e.value.status == status, kw
+    bad = K.make_conv_pool(FAKE, 256, 8, 12288, 4, K.KDA_BF16)  # pages smaller than a window
+    with pytest.raises(K.KdaError) as e:
+        K.kda_short_conv_update(bad, FAKE, FAKE, FAKE + 4096, FAKE, FAKE, n=4, out_dtype=K.KDA_BF16,
+                                stream=0)
+    assert e.value.status == K.KDA_ERR_POOL
+    # n = 0: nothing to do
+    K.kda_short_conv_update(cp, FAKE, FAKE, FAKE + 4096, FAKE, FAKE, n=0, out_dtype=K.KDA_BF16,
+                            stream=0)
+
+
 def test_noalloc_rejects_calls_above_the_static_scratch():
     """kda_prefill_chunked_noalloc rejects, before any device access, a call
     whose tables and one-chunk window exceed its static scratch (512 heads:

@@ -185,6 +185,129 @@ def test_conv_split_and_resume_bitwise():
         assert np.array_equal(cp.window_bits(p)[0], cp.window_bits(0)[0])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv_decode_shape(dtype):
+    """The decode-step update: 256 requests of one token each over the fused
+    q|k|v channels (12,288), width 4, every request entering with its window
+    page and writing its new window to a fresh page; requests whose token lands
+    on a 512 boundary also write a checkpoint window.  Outputs within the
+    rounding bound of the oracle, windows bit-exact, and three such steps
+    (pages alternating) equal one 3-token call bit for bit."""
+    W, C, n = 4, 3 * 32 * 128, 256
+    if dtype == "f32":
+        C //= 2
+    rng = np.random.default_rng(17)
+    starts = [int(x) for x in rng.integers(1, 4000, n)]
+    for r in range(0, n, 37):
+        starts[r] = 512 * (1 + r % 5) - 1  # the token ends at a 512 boundary
+    cu = np.arange(n + 1, dtype=np.int64)
+    x = G.conv_inputs(81, n, C, dtype)
+    w = G.conv_weights(81, C, W)
+    x64, w64 = to64(x, dtype), w.astype(np.float64)
+    wins = G.conv_inputs(82, n * (W - 1), C, dtype)
+    ck_req = [r for r in range(n) if (starts[r] + 1) % 512 == 0]
+    cp = ConvPool(2 * n + len(ck_req), C, W, dtype)
+    windows_in = []
+    for r in range(n):
+        v = to64(wins[r * (W - 1):(r + 1) * (W - 1)], dtype)
+        cp.set_window(r, v)
+        windows_in.append(v)
+    ckpt_cu = np.zeros(n + 1, np.int32)
+    for r in ck_req:
+        ckpt_cu[r + 1:] += 1
+    ckpt_pos = [starts[r] + 1 for r in ck_req]
+    ckpt_page = [2 * n + i for i in range(len(ck_req))]
+    y = run_conv(cp, dev(x, dtype), torch.from_numpy(w).cuda(), cu, dtype, start_pos=starts,
+                 state_in_page=list(range(n)), state_out_page=list(range(n, 2 * n)),
+                 ckpt_cu=ckpt_cu, ckpt_pos=ckpt_pos, ckpt_page=ckpt_page)
+    ref, finals, ck = conv.short_conv_varlen(x64, w64, cu, starts, windows_in,
+                                             [[starts[r] + 1] if r in ck_req else [] for r in range(n)])
+    bound = err_bound(x64, w64, cu, windows_in, dtype, ref)
+    assert not (np.abs(y - ref) > bound).any()
+    for r in range(n):
+        check_windows(cp, n + r, finals[r], f"window of request {r}")
+    for i, r in enumerate(ck_req):
+        check_windows(cp, 2 * n + i, ck[r][0], f"checkpoint window of request {r}")
+    # three decode steps, pages alternating, against one 3-token call per request
+    xs = G.conv_inputs(83, 3 * 8, C, dtype)
+    wd = torch.from_numpy(w).cuda()
+    cp2 = ConvPool(4 * 8, C, W, dtype)
+    for r in range(8):  # pages 0-7 for the steps (rewritten by step 1), 24-31 for the single call
+        cp2.set_window(r, windows_in[r])
+        cp2.set_window(24 + r, windows_in[r])
+    outs = []
+    for t in range(3):
+        xt = np.ascontiguousarray(xs.reshape(8, 3, C)[:, t])
+        outs.append(run_conv(cp2, dev(xt, dtype), wd, np.arange(9, dtype=np.int64), dtype,
+                             start_pos=[starts[r] + 1 + t for r in range(8)],
+                             state_in_page=[(t % 2) * 8 + r for r in range(8)],
+                             state_out_page=[((t + 1) % 2) * 8 + r for r in range(8)]))
+    one = run_conv(cp2, dev(xs, dtype), wd, np.arange(0, 25, 3, dtype=np.int64), dtype,
+                   start_pos=[starts[r] + 1 for r in range(8)], state_in_page=list(range(24, 32)),
+                   state_out_page=list(range(16, 24)))
+    assert np.array_equal(np.stack(outs, 1).reshape(24, C), one)
+    for r in range(8):
+        assert np.array_equal(cp2.window_bits(8 + r)[0], cp2.window_bits(16 + r)[0])
+
+
+@pytest.mark.parametrize("dtype,W", [("bf16", 4), ("f32", 3), ("bf16", 2)])
+def test_conv_update_matches_short_conv(dtype, W):
+    """kda_short_conv_update (device page tables, one token per request) gives
+    the bits of kda_short_conv on the same 1-token sequences: y and the new
+    windows; in place (page_out == page_in) as well; a request with a page
+    index outside the pool gets NaN outputs and touches no page; outputs match
+    the oracle within the rounding bound."""
+    C, n = 3 * 32 * 128 // (1 if dtype == "bf16" else 2), 200
+    x = G.conv_inputs(91 + W, n, C, dtype)
+    w = G.conv_weights(91 + W, C, W)
+    wins = G.conv_inputs(92 + W, n * (W - 1), C, dtype)
+    wd = torch.from_numpy(w).cuda()
+    xd = dev(x, dtype)
+    cp = ConvPool(3 * n + 1, C, W, dtype)
+    win64 = [to64(wins[r * (W - 1):(r + 1) * (W - 1)], dtype) for r in range(n)]
+    for r in range(n):
+        cp.set_window(r, win64[r])
+        cp.set_window(2 * n + r, win64[r])
+    ref_y = run_conv(cp, xd, wd, np.arange(n + 1, dtype=np.int64), dtype, start_pos=[7] * n,
+                     state_in_page=list(range(n)), state_out_page=list(range(n, 2 * n)))
+    # out of place: windows 0..n-1 -> fresh pages (the last request's page is invalid)
+    cp2 = ConvPool(3 * n + 1, C, W, dtype)
+    for r in range(n):
+        cp2.set_window(r, win64[r])
+    before = cp2.buf.cpu().numpy().copy()
+    y = torch.full((n, C), float("nan"), device="cuda",
+                   dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    pout = torch.arange(n, 2 * n, dtype=torch.int32, device="cuda")
+    pout[n - 1] = 3 * n + 5  # outside the pool
+    K.kda_short_conv_update(cp2.pool, xd, wd, y, pin, pout)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got[:n - 1], ref_y[:n - 1])
+    assert np.all(np.isnan(got[n - 1]))
+    for r in range(n - 1):
+        assert np.array_equal(cp2.window_bits(n + r)[0], cp.window_bits(n + r)[0]), r
+    after = cp2.buf.cpu().numpy().reshape(3 * n + 1, -1)
+    assert np.array_equal(after[2 * n - 1:], before.reshape(3 * n + 1, -1)[2 * n - 1:])
+    assert np.array_equal(after[:n], before.reshape(3 * n + 1, -1)[:n])  # inputs unchanged
+    # in place on pages 2n .. 3n-1
+    y2 = torch.empty_like(y)
+    pio = torch.arange(2 * n, 3 * n, dtype=torch.int32, device="cuda")
+    K.kda_short_conv_update(cp.pool, xd, wd, y2, pio, pio)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.float().cpu().numpy().astype(np.float64), ref_y)
+    for r in range(n):
+        assert np.array_equal(cp.window_bits(2 * n + r)[0], cp.window_bits(n + r)[0]), r
+    # against the oracle
+    x64, w64 = to64(x, dtype), w.astype(np.float64)
+    cu = np.arange(n + 1)
+    ref, finals, _ = conv.short_conv_varlen(x64, w64, cu, [7] * n, win64)
+    bound = err_bound(x64, w64, cu, win64, dtype, ref)
+    assert not (np.abs(ref_y - ref) > bound).any()
+    for r in range(n):
+        check_windows(cp, n + r, finals[r], f"window of request {r}")
+
+
 def test_conv_full_size_8k():
     """The bench workload: the fused q|k|v projection of 8192 tokens
     (3 x 32 heads x 128 channels), width 4, a checkpoint at every 512-token
