@@ -19,7 +19,9 @@ import numpy as np
 import torch  # noqa: F401  (device memory and streams)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkda.so")
+# KDA_LIBRARY selects another build of the same library (the sanitizer build
+# of build_sanitized.py for CPU test runs)
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE = 0, 1, 2, 3
 KDA_ERR_PAGE_RANGE, KDA_ERR_PAGE_ALIAS, KDA_ERR_CKPT_ALIGN, KDA_ERR_CKPT_RANGE = 4, 5, 6, 7

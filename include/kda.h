@@ -80,7 +80,11 @@ typedef enum {
   KDA_ERR_NOT_FOUND = 13   /* prefix index: no entry for that page / pin handle    */
 } kda_status;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+/* Element-type code of tensors and pools: an int32_t, so that a caller may
+ * pass any value and get KDA_ERR_DTYPE for an unknown one (a C++ enum object
+ * may not hold values outside its enumerators). */
+typedef int32_t kda_dtype;
+enum { KDA_F32 = 0, KDA_BF16 = 1 };
 
 /*
  * Paged state pool [PAGE].  `base` is device memory of num_pages * page_bytes

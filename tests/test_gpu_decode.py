@@ -16,8 +16,11 @@ TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def _run_decode(n, H, D, steps, dtype, seed, pool_pages, page_table, sample, check_steps,
-                in_place=True):
-    """Returns (max err o, max err state) over the sampled (request, head) pairs."""
+                in_place=True, all_pairs=False):
+    """Returns (max err o, max err state) over the sampled (request, head) pairs.
+    With all_pairs, every (request, head) pair is also checked on o at every
+    step and on the state after the last step (the sample's states are checked
+    at every step of check_steps)."""
     s0 = G.random_states(seed, n, H, D)  # float32 [n, H, D, D]
     pb = PoolBuf(pool_pages, H, D, page_bytes=0)
     for r in range(n):
@@ -58,6 +61,19 @@ def _run_decode(n, H, D, steps, dtype, seed, pool_pages, page_table, sample, che
     err_o = max(rel_fro(o_np[:, j], ref["o"][:, j]) for j in range(len(sample)))
     err_s = max(rel_fro(snaps[c][(r, h)], ref["ckpts"][m, j])
                 for m, c in enumerate(cks) for j, (r, h) in enumerate(sample))
+    if all_pairs:
+        # pair j = r * H + h: the steps of that (request, head) as one oracle head
+        print(f"decode: oracle on all {n * H} pairs x {steps} steps", flush=True)
+        flat = {k: d[k].reshape(steps, n * H, *d[k].shape[2:]) for k in ("q", "k", "v", "g")}
+        flat["beta"] = d["beta"].reshape(steps, n * H)
+        ref = oracle.run(flat["q"], flat["k"], flat["v"], flat["g"], flat["beta"], [0, steps],
+                         s0=s0.reshape(1, n * H, D, D).astype(np.float64))
+        o_full = o_all.reshape(steps, n * H, D).double().cpu().numpy()
+        err_o = max(err_o, max(rel_fro(o_full[:, j], ref["o"][:, j]) for j in range(n * H)))
+        del o_full
+        for r in range(n):
+            st = pb.states(int(pin[r] if not in_place else page_table[r]))
+            err_s = max(err_s, max(rel_fro(st[h], ref["s_final"][0, r * H + h]) for h in range(H)))
     return err_o, err_s
 
 
@@ -80,18 +96,18 @@ def test_decode_ping_pong_pages():
     assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], (e_o, e_s)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_decode_256_full():
     """256 requests x 32 heads x d=128, 1000 consecutive steps in place through a
-    random page table of a 512-page pool; 48 sampled (request, head) pairs are
-    checked against the oracle on o at every step and on the state after steps
-    1, 10, 100 and 1000."""
+    random page table of a 512-page pool.  All 8192 (request, head) pairs are
+    checked against the oracle on o at every step and on the state after step
+    1000; 48 sampled pairs also on the states after steps 1, 10 and 100."""
     w = G.DECODE_256
     pt = G.decode_page_table(w)
     rng = np.random.default_rng(1)
     sample = [(int(r), int(h)) for r, h in zip(rng.integers(0, w.n_req, 48), rng.integers(0, w.H, 48))]
     e_o, e_s = _run_decode(w.n_req, w.H, w.D, w.steps, w.dtype, w.seed, w.pool_pages, pt, sample,
-                           {1, 10, 100, 1000})
+                           {1, 10, 100, 1000}, all_pairs=True)
     assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], (e_o, e_s)
 
 
