@@ -191,16 +191,41 @@ def ckpt_plan(start, length, hash_block):
 
 
 def longest_certified_boundary(model: PrefixIndexModel, tokens):
-    """Independent restatement of the hit for pins: the largest b (multiple of
-    the hash block, b <= n) such that (1) tokens[0:b] is covered by ready page
-    prefixes in the two-stage sense and (2) a complete ready checkpoint holds
-    exactly tokens[0:b].  Scans every registered checkpoint prefix instead of
-    walking boundaries."""
+    """Independent restatement of the hit, for pins: the largest b (multiple of
+    the hash block, b <= n) such that
+
+    (1) MLA covers tokens[0:b]: with R the set of lengths L for which a ready
+        page is registered under exactly tokens[0:L], every whole physical page
+        before the one holding token b-1 ends in R (k * pb in R for
+        k = 1 .. i, i = (b-1) // pb), and some hash-block end e in R lies in
+        page i at or after b (b <= e <= min((i+1) * pb, full), full = the
+        request's last hash-block end);
+    (2) a complete ready checkpoint holds exactly tokens[0:b].
+
+    Computed from the registered entries directly (R by scanning every page
+    entry; candidates by scanning every checkpoint), sharing no code with the
+    model's lookup walk."""
     tokens = tuple(int(t) for t in tokens)
-    mla, _ = model.mla_match(tokens)
+    n = len(tokens)
+    hb, pb = model.hb, model.pb
+    full = n // hb * hb
+    R = set()
+    for e in model.pages.values():
+        L = len(e["prefix"])
+        if e["ready"] and 0 < L <= n and tokens[:L] == e["prefix"]:
+            R.add(L)
+
+    def covered(b):
+        i = (b - 1) // pb
+        if any(k * pb not in R for k in range(1, i + 1)):
+            return False
+        top = min((i + 1) * pb, full)
+        return any(e in R for e in range(b, top + 1) if e % hb == 0)
+
     best = 0
     for prefix, c in model.ckpts.items():
         b = len(prefix)
-        if c["ready"] and min(c["pages"]) >= 0 and b <= mla and tokens[:b] == prefix:
-            best = max(best, b)
+        if (c["ready"] and min(c["pages"]) >= 0 and 0 < b <= n and b % hb == 0
+                and tokens[:b] == prefix and b > best and covered(b)):
+            best = b
     return best

@@ -152,3 +152,62 @@ def test_two_restatements_agree_on_random_workloads():
         for cut in (1200, 1300, len(t) // 2, len(t)):
             r = np.concatenate([t[:cut], seq(50, 999) + 400_000])
             assert m.lookup(r)["boundary"] == longest_certified_boundary(m, r)
+
+
+def _partial_page_workload():
+    """A conversation whose last page is partial (2100 tokens in 1536-token
+    pages: page 1 registered under its last complete hash block, 2048), a
+    checkpoint at every hash block, and requests diverging inside page 1."""
+    hb, pb, G = 512, 1536, 2
+    m = PrefixIndexModel(hb, pb, G)
+    t = seq(2100, 31)
+    m.register_pages(t, [0, 1], step=0)
+    for b in range(hb, 2100 + 1, hb):
+        for g in range(G):
+            m.register_ckpt(t, b, g, 100 + 2 * b + g, True, 0)
+    m.mark_ready(0)
+    reqs = [np.concatenate([t[:cut], seq(40, 77) + 500_000]) for cut in (2100, 2060, 1900, 1600)]
+    return m, reqs
+
+
+def test_certifier_catches_mla_stage_mistakes(monkeypatch):
+    """The certifier restates the MLA stage on its own: planted mistakes in the
+    model's MLA walk (the partial-page stage dropped; its scan starting one hash
+    block too low) make the two disagree, while the model as written agrees."""
+    m, reqs = _partial_page_workload()
+    assert [m.lookup(r)["boundary"] for r in reqs] == [2048, 2048, 1536, 1536]
+    assert all(m.lookup(r)["boundary"] == longest_certified_boundary(m, r) for r in reqs)
+    orig = PrefixIndexModel.mla_match
+
+    def no_partial(self, tokens):
+        mla, pages = orig(self, tokens)
+        whole = mla // self.pb * self.pb
+        return whole, pages[:whole // self.pb]
+
+    def low_scan(self, tokens):
+        # the walk as written, except that the partial-page scan starts one
+        # hash block below the request's last complete hash-block end
+        n = len(tokens)
+        full = n // self.hb * self.hb
+        pages, i = [], 0
+        while True:
+            pend = (i + 1) * self.pb
+            if pend <= full:
+                p = self._served(tokens, pend)
+                if p is not None:
+                    pages.append(p)
+                    i += 1
+                    continue
+            for e in range(min(pend - self.hb, full) - self.hb, i * self.pb, -self.hb):
+                p = self._served(tokens, e)
+                if p is not None:
+                    pages.append(p)
+                    return e, pages
+            return i * self.pb, pages
+
+    for mutant in (no_partial, low_scan):
+        monkeypatch.setattr(PrefixIndexModel, "mla_match", mutant)
+        assert any(m.lookup(r)["boundary"] != longest_certified_boundary(m, r) for r in reqs), \
+            mutant.__name__
+    monkeypatch.setattr(PrefixIndexModel, "mla_match", orig)
+
