@@ -162,6 +162,60 @@ def summarize_util(util_dir, command):
     return "\n".join(lines) + "\n"
 
 
+def summarize_trace(kt_dir, bench_json, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script
+    (its kernel_stats.csv) next to the HIP-event figures the same run printed
+    (its JSON line, saved to a file)."""
+    stats = sorted(glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True))
+    rows = list(csv.DictReader(open(stats[0]))) if stats else []
+    with open(bench_json) as f:
+        b = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    lines = [
+        "# Kernel-trace summary: bench.py core workloads (8K prefill, 256x32 decode, 256-page copy,",
+        "# int8 checkpoints, verify, short conv and its decode-shaped update)", "",
+        "Commands (on an MI355X, from /tmp with TMPDIR=/tmp, R = repository root, OUT = the profiler's",
+        "output directory):", "", "```", *command, "```", "",
+        "Workloads: prefill H=32, d=128, T=8192, bf16 in / fp32 state, checkpoints {2560, 6144, 8192}, run",
+        "as two windows of 64 chunks (two prep and two scan launches per call); decode 256 requests x 32",
+        "heads in place; copy 256 x 2 MiB pages; int8 checkpoint write and restore of 256 pages x 32",
+        "heads; speculative verify 128 requests x 4 tokens; short conv 8192 x 12288 bf16, width 4; conv",
+        "update 256 requests x 12288 channels x 1 token.", "",
+        "| Kernel | Calls | Average (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 60:
+            name = name[:57] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    lines += ["", "Same-run HIP-event figures (library event pairs on the launch stream):", ""]
+    for k, v in b.get("kernels_diagnostic", {}).items():
+        lines.append(f"- {k}: {1e3 * v['avg_ms']:.1f} us per launch, {v['launches_per_call']:.0f} per call")
+    r = b["roofline"]
+    lines.append(f"- prefill step: {b['ms_per_step'] * 1e3:.0f} us, {b['value'] / 1e6:.2f} M tokens/s; "
+                 f"{100 * r['frac']:.1f}% of HBM, {100 * r['frac_mfma_bf16']:.1f}% of bf16 MFMA "
+                 f"(this run; the profiler adds a few us per launch)")
+    for tag, key in (("decode", "decode"), ("copy", "checkpoint_copy"), ("verify", "verify"),
+                     ("conv", "short_conv")):
+        d = b.get(key)
+        if d:
+            lines.append(f"- {tag}: kernel {1e3 * d['kernel_avg_ms']:.1f} us ({d['kernel_gbps']:.0f} GB/s, "
+                         f"{100 * d['frac_hbm']:.1f}% of 8 TB/s)")
+    d = b.get("checkpoint_int8")
+    if d:
+        for part in ("write", "restore"):
+            p = d[part]
+            lines.append(f"- int8 {part}: kernel {1e3 * p['kernel_avg_ms']:.1f} us ({p['kernel_gbps']:.0f} GB/s, "
+                         f"{100 * p['frac_hbm']:.1f}% of 8 TB/s)")
+    d = b.get("short_conv_decode")
+    if d:
+        for part in ("update", "short_conv_1tok_seqs"):
+            p = d[part]
+            lines.append(f"- conv decode ({part}): {1e3 * p['ms_per_call']:.1f} us per call, kernel "
+                         f"{1e3 * p['kernel_avg_ms']:.1f} us ({100 * p['frac_hbm']:.1f}% of 8 TB/s)")
+    return "\n".join(lines) + "\n"
+
+
 def to_dev(x, dtype):
     import torch
     if dtype == "bf16":
@@ -652,9 +706,17 @@ def main():
                     help="skip the resume and 2^20-token workloads (profiling runs: one prefill shape)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the markdown traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KT_DIR", "BENCH_JSON"),
+                    help="print the markdown summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-util", metavar="UTIL_DIR",
                     help="print the markdown summary of a rocprofv3 --pmc run of UTIL_COUNTERS and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        cmd = ["rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run -- "
+               "python3 $R/bench.py --steps 20 --warmup 2 --no-cpu --only-core > $OUT/kt_bench.json",
+               "python3 $R/bench.py --summarize-trace $OUT/kt $OUT/kt_bench.json"]
+        sys.stdout.write(summarize_trace(*args.summarize_trace, cmd))
+        return
     if args.summarize_util:
         cmd = [f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d $OUT/pmc_util "
                f"-o run -- python3 $R/bench.py --steps 3 --warmup 1 --no-cpu --only-core",
