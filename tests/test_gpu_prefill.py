@@ -99,6 +99,7 @@ def _const(x, dtype, value):
 
 @pytest.mark.parametrize("dtype,g_lo,g_hi", [
     ("bf16", -1.2, 0.0), ("f32", -1.2, 0.0),   # strong, mixed decay
+    ("bf16", -3.0, 0.0), ("f32", -3.0, 0.0),   # chunk sums near -96
     ("bf16", -2.7, -2.6), ("f32", -2.7, -2.6),  # edge: ~86 of log-decay per half chunk
 ])
 def test_strong_decay(dtype, g_lo, g_hi):
