@@ -326,6 +326,9 @@ template <int D> struct Prep2Layout {
   static constexpr int kBytes = kBeta + 64 * 4;
   static_assert(kBytes <= 80 * 1024, "two workgroups must fit in one CU's LDS");
   static_assert(kRQ % 16 == 0 && kRT % 16 == 0 && kBytes % 16 == 0, "align");
+  // the workspace Qt staged in the Qt' region: 64 * D / 8 units of 16 bytes,
+  // 16 bytes of padding after every 16 units
+  static_assert(64 * D * 2 + 64 * D * 2 / 16 <= kTileK, "Qt staging fits the Qt' region");
 };
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
@@ -480,6 +483,10 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
   }
   __syncthreads();  // partials are overwritten by Kt^T below
 
+  // workspace Qt of this thread's channel pair, rows r0 .. r0+TPP-1: staged
+  // through LDS after the Gram products (see phase E)
+  uint32_t qs[TPP];
+
   // ---- C: decayed tiles --------------------------------------------------------
   // The Gram tiles (LDS) are decayed relative to the mid-chunk prefix G_31:
   // Kt' = K exp(G - G_31), Kh' = K exp(G_31 - G), Qt' = Q exp(G - G_31), whose
@@ -511,8 +518,7 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
         *reinterpret_cast<uint32_t*>(Kt + r * LDK + c0) = pack_bf16x2(kt0, kt1);
         *reinterpret_cast<uint32_t*>(Kh + r * LDK + c0) = pack_bf16x2(kh0, kh1);
         *reinterpret_cast<uint32_t*>(Qt + r * LDK + c0) = pack_bf16x2(qt0, qt1);
-        *reinterpret_cast<uint32_t*>(at32(out, IO::kQt + frag_off<32>(r, c0, D))) =
-            pack_bf16x2(qt0 * eM0, qt1 * eM1);
+        qs[i + u] = pack_bf16x2(qt0 * eM0, qt1 * eM1);
       }
       ktT0[i / 2] = lo_halves(kt2[0], kt2[1]);
       ktT1[i / 2] = hi_halves(kt2[0], kt2[1]);
@@ -567,7 +573,15 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
         }
       }
     }
-    __syncthreads();  // Kt/Kh are overwritten by L below
+    __syncthreads();  // Kt/Kh are overwritten by L below; Qt' is free
+    // workspace Qt -> the Qt' region, in the workspace's fragment-major order
+    // with 16 bytes of padding after every 256 (so that the 16 units one
+    // instruction writes, 256 bytes apart, fall in different banks)
+#pragma unroll
+    for (int i = 0; i < TPP; ++i) {
+      const int e = frag_off<32>(r0 + i, c0, D);  // element; its 16-byte unit is e / 8
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(Qt) + 2 * e + 16 * (e >> 7)) = qs[i];
+    }
     const int jq = 4 * (lane >> 4);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -619,6 +633,18 @@ __global__ __launch_bounds__(256) void prep2_kernel(PrepArgs a, int total_pairs)
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) Ti[(b0 + i) * LDF + b0 + j] = x[i];
+  } else {
+    // meanwhile waves 1..3 store the staged workspace Qt: 16-byte units in
+    // order, 1 KB of contiguous workspace per wave instruction
+    constexpr int kUnits = 64 * D / 8;
+    const uint8_t* stage = reinterpret_cast<const uint8_t*>(Qt);
+#pragma unroll
+    for (int k = 0; k < (kUnits + 191) / 192; ++k) {
+      const int u = 192 * k + (t - 64);
+      if (u < kUnits)
+        *reinterpret_cast<u32x4_t*>(at32(out, IO::kQt + 8 * u)) =
+            *reinterpret_cast<const u32x4_t*>(stage + 16 * u + 16 * (u >> 4));
+    }
   }
   __syncthreads();
   // C tile (16x16) -> Ti block (row block rb, col block cb), optionally negated
@@ -864,13 +890,6 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   const int n_lo = max(a.c0 - se.chunk_begin, 0);
   const int n_hi = min(a.c0 + a.nch - se.chunk_begin, nchunks);
 
-  CO f0, f1, f2, f3;
-  if (n_hi > n_lo) {
-    load_ops<D, Op, NH>(f0, c, n_lo);
-    if (PF >= 2) load_ops<D, Op, NH>(f1, c, min(n_lo + 1, n_hi - 1));
-    if (PF >= 3) load_ops<D, Op, NH>(f2, c, min(n_lo + 2, n_hi - 1));
-  }
-
   // this wave's S tiles: rows 16*wv + 4*(lane/16) + r, column c0 + 16*j + lane%16;
   // the entering state is the sequence's (first window) or the carried one
   f32x4 S[NH];
@@ -908,6 +927,18 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
     }
   };
   auto s_store = [&](int page) { s_store_to(reinterpret_cast<float*>(a.pool + page * a.page_bytes) + hoff); };
+
+  // The chunk loop is reachable only through the operand prologue, which is
+  // issued after the state loads.  The wait counts inside the loop are derived
+  // from every path into it: a path on which the state loads were the latest
+  // memory operations (no prologue) made the loop's first use of S wait for
+  // nearly every load in flight, on every iteration (3% of the scan's time).
+  if (n_hi > n_lo) {
+  __builtin_amdgcn_sched_barrier(0);
+  CO f0, f1, f2, f3;
+  load_ops<D, Op, NH>(f0, c, n_lo);
+  if (PF >= 2) load_ops<D, Op, NH>(f1, c, min(n_lo + 1, n_hi - 1));
+  if (PF >= 3) load_ops<D, Op, NH>(f2, c, min(n_lo + 2, n_hi - 1));
   s_to_lds();
 
   int nck = se.ckpt_begin;
@@ -1066,6 +1097,7 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   }
   (void)f2;
   (void)f3;
+  }
   if (n_hi < nchunks) s_store_to(a.carry_out + hoff);  // continues in the next window
   else if (se.state_out >= 0) s_store(se.state_out);
 }
