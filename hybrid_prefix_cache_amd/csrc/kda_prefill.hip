@@ -849,7 +849,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   using OT = OpT<Op>;
   using CO = ChunkOps<D, Op, NH>;
   constexpr int BW = 16 * NH, NS = D / BW, KK = OT::kK;
-  constexpr int PF = sizeof(Op) == 2 ? 3 : 1;  // chunks of operands prefetched ahead
+  // chunks of operands prefetched ahead (bf16: two, 157 registers; three
+  // took 194 and were no faster)
+  constexpr int PF = sizeof(Op) == 2 ? 2 : 1;
   // bf16: the few LDS operand fragments of a product are read up front (fp32
   // has 8x as many fragments; they are read as the products go)
   constexpr bool kBatchLds = sizeof(Op) == 2;
@@ -935,10 +937,9 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   // nearly every load in flight, on every iteration (3% of the scan's time).
   if (n_hi > n_lo) {
   __builtin_amdgcn_sched_barrier(0);
-  CO f0, f1, f2, f3;
+  CO f0, f1, f2;
   load_ops<D, Op, NH>(f0, c, n_lo);
   if (PF >= 2) load_ops<D, Op, NH>(f1, c, min(n_lo + 1, n_hi - 1));
-  if (PF >= 3) load_ops<D, Op, NH>(f2, c, min(n_lo + 2, n_hi - 1));
   s_to_lds();
 
   int nck = se.ckpt_begin;
@@ -1078,16 +1079,14 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
   };
 
   int n = n_lo;
-  if constexpr (PF == 3) {
-    for (; n + 4 <= n_hi; n += 4) {
-      step(f0, f3, n);
+  if constexpr (PF == 2) {
+    for (; n + 3 <= n_hi; n += 3) {
+      step(f0, f2, n);
       step(f1, f0, n + 1);
       step(f2, f1, n + 2);
-      step(f3, f2, n + 3);
     }
-    if (n < n_hi) step(f0, f3, n);
+    if (n < n_hi) step(f0, f2, n);
     if (n + 1 < n_hi) step(f1, f0, n + 1);
-    if (n + 2 < n_hi) step(f2, f1, n + 2);
   } else {
     for (; n + 2 <= n_hi; n += 2) {
       step(f0, f1, n);
@@ -1096,7 +1095,6 @@ __global__ __launch_bounds__(512) void scan_kernel(ScanArgs a) {
     if (n < n_hi) step(f0, f1, n);
   }
   (void)f2;
-  (void)f3;
   }
   if (n_hi < nchunks) s_store_to(a.carry_out + hoff);  // continues in the next window
   else if (se.state_out >= 0) s_store(se.state_out);
