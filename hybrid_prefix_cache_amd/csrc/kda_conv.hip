@@ -174,83 +174,96 @@ __global__ __launch_bounds__(256) void conv_kernel(ConvArgs a) {
   }
 }
 
-// Decode-step update: one token per request.  Workgroup (request r, column of
-// 256 channel groups); the thread reads the request's window (W-1 rows of its
-// 16-byte channel group) from page_in[r] and the token row of x, writes y and
-// the shifted window (the last W-2 window rows and the token) to page_out[r].
-// Every load precedes every store in the thread, so page_out[r] may equal
+// Decode-step update: one token per request.  Workgroup (R consecutive
+// requests, column of 256 channel groups): the thread loads the taps of its
+// 16-byte channel group once, then for each of its requests reads the window
+// (W-1 rows) from page_in[r] and the token row of x, writes y and the shifted
+// window (the last W-2 window rows and the token) to page_out[r].  All loads
+// of the R requests are issued before any store, so page_out[r] may equal
 // page_in[r].  A page index outside the pool touches no page and gives NaN
 // outputs.  Same taps and summation order as conv_kernel: bit-identical
 // outputs and windows for the same inputs.
+constexpr int kConvUpdateReqs = 4;  // requests per workgroup
+
 template <typename In, int W>
 __global__ __launch_bounds__(256) void conv_update_kernel(ConvUpdateArgs a) {
   using CV = ConvVec<In>;
-  constexpr int N = CV::N;
-  const int r = blockIdx.x;
+  constexpr int N = CV::N, R = kConvUpdateReqs;
+  const int r0 = blockIdx.x * R;
   const int c0 = (blockIdx.y * 256 + threadIdx.x) * N;
   if (c0 >= a.C) return;
   const int64_t C = a.C;
-  const int pin = a.page_in[r], pout = a.page_out[r];  // uniform: scalar loads
-  const int64_t yo = (int64_t)r * C + c0;
-  if (pin < 0 || pin >= a.num_pages || pout < 0 || pout >= a.num_pages) {
-    const float nan = __builtin_nanf("");
-    if (a.out_bf16) {
-      u32x4_t q = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-      if constexpr (N == 8) *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.y) + yo) = q;
-      else *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.y) + yo) = u32x2_t{q[0], q[1]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < N; i += 4)
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + yo + i) = f32x4{nan, nan, nan, nan};
-    }
-    return;
-  }
   float wt[W][N];
 #pragma unroll
   for (int i = 0; i < N; ++i)
 #pragma unroll
     for (int j = 0; j < W; ++j) wt[j][i] = a.w[(int64_t)(c0 + i) * W + j];
-  const In* sp = reinterpret_cast<const In*>(a.cpool + (int64_t)pin * a.cpage_bytes);
-  u32x4_t rows[W];
+  bool ok[R];
+  int pout[R];
+  u32x4_t rows[R][W];
 #pragma unroll
-  for (int j = 0; j < W - 1; ++j) rows[j] = CV::raw(sp + (int64_t)j * C + c0);
-  rows[W - 1] = CV::raw(reinterpret_cast<const In*>(a.x) + yo);
-  float yv[N];
+  for (int q = 0; q < R; ++q) {
+    const int r = r0 + q;
+    ok[q] = false;
+    pout[q] = 0;
+    if (r >= a.n) continue;
+    const int pin = a.page_in[r], po = a.page_out[r];  // uniform: scalar loads
+    ok[q] = pin >= 0 && pin < a.num_pages && po >= 0 && po < a.num_pages;
+    pout[q] = po;
+    if (!ok[q]) continue;
+    const In* sp = reinterpret_cast<const In*>(a.cpool + (int64_t)pin * a.cpage_bytes);
 #pragma unroll
-  for (int i = 0; i < N; ++i) yv[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < W; ++j) {
-    float xv[N];
-    CV::unpack(rows[j], xv);
-#pragma unroll
-    for (int i = 0; i < N; ++i) yv[i] = fmaf(wt[j][i], xv[i], yv[i]);
+    for (int j = 0; j < W - 1; ++j) rows[q][j] = CV::raw(sp + (int64_t)j * C + c0);
+    rows[q][W - 1] = CV::raw(reinterpret_cast<const In*>(a.x) + (int64_t)r * C + c0);
   }
-  if (a.out_bf16) {
-    u32x4_t q;
 #pragma unroll
-    for (int i = 0; i < N / 2; ++i) q[i] = pack_bf16x2(yv[2 * i], yv[2 * i + 1]);
-    if constexpr (N == 8) {
-      __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.y) + yo));
+  for (int q = 0; q < R; ++q) {
+    const int r = r0 + q;
+    if (r >= a.n) continue;
+    const int64_t yo = (int64_t)r * C + c0;
+    float yv[N];
+    if (ok[q]) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) yv[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        float xv[N];
+        CV::unpack(rows[q][j], xv);
+#pragma unroll
+        for (int i = 0; i < N; ++i) yv[i] = fmaf(wt[j][i], xv[i], yv[i]);
+      }
     } else {
-      __builtin_nontemporal_store(u32x2_t{q[0], q[1]},
-                                  reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.y) + yo));
+#pragma unroll
+      for (int i = 0; i < N; ++i) yv[i] = __builtin_nanf("");
     }
-  } else {
+    if (a.out_bf16) {
+      u32x4_t qv;
 #pragma unroll
-    for (int i = 0; i < N; i += 4)
-      __builtin_nontemporal_store(f32x4{yv[i], yv[i + 1], yv[i + 2], yv[i + 3]},
-                                  reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + yo + i));
+      for (int i = 0; i < N / 2; ++i) qv[i] = pack_bf16x2(yv[2 * i], yv[2 * i + 1]);
+      if constexpr (N == 8) {
+        __builtin_nontemporal_store(qv, reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(a.y) + yo));
+      } else {
+        __builtin_nontemporal_store(u32x2_t{qv[0], qv[1]},
+                                    reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(a.y) + yo));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; i += 4)
+        __builtin_nontemporal_store(f32x4{yv[i], yv[i + 1], yv[i + 2], yv[i + 3]},
+                                    reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.y) + yo + i));
+    }
+    if (!ok[q]) continue;
+    uint8_t* dp = a.cpool + (int64_t)pout[q] * a.cpage_bytes + (int64_t)c0 * sizeof(In);
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j)
+      *reinterpret_cast<u32x4_t*>(dp + (int64_t)j * C * sizeof(In)) = rows[q][j + 1];
   }
-  uint8_t* dp = a.cpool + (int64_t)pout * a.cpage_bytes + (int64_t)c0 * sizeof(In);
-#pragma unroll
-  for (int j = 0; j < W - 1; ++j)
-    *reinterpret_cast<u32x4_t*>(dp + (int64_t)j * C * sizeof(In)) = rows[j + 1];
 }
 
 template <typename In>
 static hipError_t launch_conv_update_t(const ConvUpdateArgs& a, hipStream_t st) {
   constexpr int N = ConvVec<In>::N;
-  const dim3 grid((unsigned)a.n, (unsigned)((a.C / N + 255) / 256));
+  const dim3 grid((unsigned)((a.n + kConvUpdateReqs - 1) / kConvUpdateReqs), (unsigned)((a.C / N + 255) / 256));
   if (a.W == 2) hipLaunchKernelGGL((conv_update_kernel<In, 2>), grid, dim3(256), 0, st, a);
   else if (a.W == 3) hipLaunchKernelGGL((conv_update_kernel<In, 3>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((conv_update_kernel<In, 4>), grid, dim3(256), 0, st, a);
