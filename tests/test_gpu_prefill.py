@@ -153,6 +153,22 @@ def test_identity_beta0_alpha1(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_out_of_domain_gates_are_not_silent(dtype):
+    """Gates past the chunk form's domain (g = -4 everywhere: a half chunk of
+    gates sums to -128, beyond the |G_i - G_31| < 87 that include/kda.h states)
+    give non-finite outputs and a non-finite state, never finite values that
+    could pass for a result.  (The recurrence itself is finite there; the
+    oracle is not consulted.)"""
+    H, D, T = 2, 128, 300
+    d = G.kda_tokens(5, H, D, 0, T, dtype)
+    d["g"] = _const(d["g"], dtype, -4.0)
+    pb = PoolBuf(2, H, D)
+    o = prefill(pb, inputs_to_dev(d, dtype), [0, T], dtype, state_out_page=[0])
+    assert not bool(torch.isfinite(o).all())
+    assert not np.isfinite(pb.states(0)).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_exact_write_beta1_unit_key(dtype):
     """beta = 1 with unit keys: the delta rule overwrites the value stored under
     the key, S_t^T k_t = v_t (up to ||k_t||^2 - 1, the rounding of the stored
