@@ -431,3 +431,11 @@ def test_prefill_host_array_lengths(kw):
 def test_copy_host_array_lengths(fn):
     with pytest.raises(ValueError):
         getattr(K, fn)(pool(), [1, 2], [3], stream=0)
+
+
+def test_c_consumer_builds(tmp_path):
+    """include/kda.h is valid C99 (no C++ needed) and a C program using it
+    links against the in-tree libkda.so (every symbol it calls resolves)."""
+    import abi_consumer_build
+    exe = abi_consumer_build.build(str(tmp_path / "abi_consumer"))
+    assert os.path.exists(exe)
