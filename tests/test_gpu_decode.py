@@ -86,6 +86,18 @@ def test_decode_small(dtype, D):
     assert e_o <= TOL[dtype] and e_s <= TOL[dtype], (e_o, e_s)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_decode_many_heads(dtype, D):
+    """96 heads (one layer's KDA heads in the pages' model), 37 requests in
+    place through a permuted page table: every (request, head) pair checked on
+    o at every step and on its state after the last step."""
+    n, H, steps = 37, 96, 20
+    pt = np.random.default_rng(3).permutation(80)[:n]
+    sample = [(0, 0), (n - 1, H - 1), (17, 50)]
+    e_o, e_s = _run_decode(n, H, D, steps, dtype, 515 + D, 80, pt, sample, {1, steps}, all_pairs=True)
+    assert e_o <= TOL[dtype] and e_s <= TOL[dtype], (e_o, e_s)
+
+
 def test_decode_ping_pong_pages():
     """page_out != page_in (alternating between two page sets) gives the same
     result as the in-place update."""

@@ -253,6 +253,38 @@ def test_resume_bitwise_and_oracle(g_lo):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_many_heads(dtype, D):
+    """96 heads (one layer's KDA heads in the pages' model): the library picks
+    32-column slabs on its own at this head count and cuts the call into windows
+    of 21 chunks, which sequences cross.  Three sequences, one entering from a
+    state at position 1024, checkpoints inside and at the ends; every head
+    compared with the oracle on o, the checkpoints and the final states."""
+    H = 96
+    cu = [0, 2900, 4100, 4800]
+    T = cu[-1]
+    d = G.kda_tokens(4242 + D, H, D, 0, T, dtype)
+    pb = PoolBuf(9, H, D)
+    rng = np.random.default_rng(11)
+    s_in = (rng.standard_normal((H, D, D)) / np.sqrt(D)).astype(np.float32).astype(np.float64)
+    pb.set_states(8, s_in)
+    start = [0, 1024, 0]
+    # absolute checkpoint positions: seq 0 at 512, 1536 and its end (2900 is no
+    # block end: only 512 and 1536 qualify), seq 1 at 1536 and 2048, seq 2 none
+    ckpt_cu, ckpt_pos, ckpt_page = [0, 2, 4, 4], [512, 1536, 1536, 2048], [3, 4, 5, 6]
+    before = pb.snapshot()
+    o = prefill(pb, inputs_to_dev(d, dtype), cu, dtype, start_pos=start, state_in_page=[-1, 8, -1],
+                state_out_page=[0, 1, 2], ckpt_cu=ckpt_cu, ckpt_pos=ckpt_pos, ckpt_page=ckpt_page)
+    s0 = np.zeros((3, H, D, D))
+    s0[1] = s_in
+    ref = _oracle_prefill(d, cu, start_pos=start, s0=s0, ckpt_cu=ckpt_cu, ckpt_pos=ckpt_pos)
+    err_o = max_rel_blocks(o.double().cpu().numpy(), ref["o"], cu, H)
+    err_c = max(rel_fro(pb.states(ckpt_page[m])[h], ref["ckpts"][m, h]) for m in range(4) for h in range(H))
+    err_s = max(rel_fro(pb.states(s)[h], ref["s_final"][s, h]) for s in range(3) for h in range(H))
+    assert max(err_o, err_c, err_s) <= TOL[dtype], (err_o, err_c, err_s)
+    assert _poison_mask_ok(before, pb.snapshot(), pb, [0, 1, 2, 3, 4, 5, 6])
+
+
 def test_in_place_and_empty_sequence_with_state():
     """state_in == state_out updates in place; a zero-length sequence with an
     entering state copies it to its output page unchanged."""
