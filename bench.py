@@ -699,6 +699,123 @@ def cpu_baseline(G, w, d):
                       f"heads), {runs} runs in {el:.2f} s"}
 
 
+def rocminfo_gpu_facts():
+    """Lines of `rocminfo` that describe the first GPU agent (name, compute
+    units, clock, SIMDs, wave size, caches), or an explanation if it fails."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError) as e:
+        return [f"rocminfo unavailable: {e}"]
+    keys = ("Marketing Name", "Compute Unit", "Max Clock Freq", "SIMDs per CU", "Wavefront Size",
+            "Max Waves Per CU", "L1", "L2", "L3", "Workgroup Max Size:")
+    facts, in_gpu = [], False
+    for line in txt.splitlines():
+        t = line.strip()
+        if t.startswith("Name:") and "gfx" in t:
+            if in_gpu:
+                break  # the second GPU agent
+            in_gpu = True
+            facts.append(t)
+            continue
+        if in_gpu and t.startswith("Agent "):
+            break
+        if in_gpu and any(t.startswith(k) for k in keys):
+            facts.append(" ".join(t.split()))
+    return facts or ["no GPU agent found in rocminfo output"]
+
+
+def measure_peaks(reps=10):
+    """Measured counterparts of the roofline denominators: a copy and a fill of
+    1 GiB (libkda_probe.so and torch's own kernels) and a loop of independent
+    bf16 MFMAs on every CU, each the median of `reps` launches timed with HIP
+    events."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "hybrid_prefix_cache_amd", "libkda_probe.so"))
+    lib.kda_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.kda_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.kda_probe_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def median_ms(launch):
+        assert launch() == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert launch() == 0
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    blocks, iters = 8 * cus, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    t_mfma = median_ms(lambda: lib.kda_probe_mfma_bf16(out.data_ptr(), blocks, iters, st))
+    flops = blocks * 4 * iters * 16 * 16384
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    t_fill = median_ms(lambda: lib.kda_probe_fill(dst.data_ptr(), nbytes, 0x3F800000, st))
+    t_copy = median_ms(lambda: lib.kda_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st))
+    assert torch.equal(dst[-4096:], src[-4096:])
+
+    def torch_ms(fn):  # the same operations through torch's own kernels
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+    t_tcopy = torch_ms(lambda: dst.copy_(src))
+    t_tfill = torch_ms(lambda: dst.fill_(7))
+    return {
+        "device": props.name, "compute_units": cus, "hbm_bytes": props.total_memory,
+        "rocminfo": rocminfo_gpu_facts(),
+        "mfma_bf16_tflops": flops / (t_mfma / 1e3) / 1e12, "mfma_ms": t_mfma, "mfma_flop": flops,
+        "copy_gbps": 2 * nbytes / (t_copy / 1e3) / 1e9, "copy_ms": t_copy,
+        "fill_gbps": nbytes / (t_fill / 1e3) / 1e9, "fill_ms": t_fill,
+        "torch_copy_gbps": 2 * nbytes / (t_tcopy / 1e3) / 1e9, "torch_copy_ms": t_tcopy,
+        "torch_fill_gbps": nbytes / (t_tfill / 1e3) / 1e9, "torch_fill_ms": t_tfill,
+    }
+
+
+def summarize_peaks(p, cmd):
+    """Markdown summary of measure_peaks() against the published peaks."""
+    lines = ["# MI355X: device facts and measured peaks next to the published ones", "",
+             f"Command (repository root, one GPU): `{cmd}`", "",
+             "The benchmark's roofline fractions use the published peaks (HBM 8 TB/s, dense bf16",
+             "MFMA 2.5 PFLOP/s); these probes show what simple kernels reach on the same part.", "",
+             "| probe | measured | published peak | fraction |", "|---|---|---|---|",
+             f"| bf16 MFMA loop ({p['mfma_flop'] / 1e12:.1f} TFLOP: 8 workgroups of 4 waves per CU, 16 "
+             f"independent v_mfma_f32_16x16x32_bf16 chains per wave) | {p['mfma_bf16_tflops']:.0f} TFLOP/s "
+             f"({p['mfma_ms']:.2f} ms) | {BF16_PEAK_TFLOPS:.0f} TFLOP/s | "
+             f"{p['mfma_bf16_tflops'] / BF16_PEAK_TFLOPS:.3f} |",
+             f"| copy, 1 GiB (read + write counted; one 16-byte non-temporal vector per thread) | "
+             f"{p['copy_gbps']:.0f} GB/s ({p['copy_ms']:.3f} ms) | {HBM_PEAK_GBS:.0f} GB/s | "
+             f"{p['copy_gbps'] / HBM_PEAK_GBS:.3f} |",
+             f"| fill, 1 GiB (same shape) | {p['fill_gbps']:.0f} GB/s ({p['fill_ms']:.3f} ms) | "
+             f"{HBM_PEAK_GBS:.0f} GB/s | {p['fill_gbps'] / HBM_PEAK_GBS:.3f} |",
+             f"| torch `copy_`, 1 GiB (read + write counted) | {p['torch_copy_gbps']:.0f} GB/s "
+             f"({p['torch_copy_ms']:.3f} ms) | {HBM_PEAK_GBS:.0f} GB/s | "
+             f"{p['torch_copy_gbps'] / HBM_PEAK_GBS:.3f} |",
+             f"| torch `fill_`, 1 GiB | {p['torch_fill_gbps']:.0f} GB/s ({p['torch_fill_ms']:.3f} ms) | "
+             f"{HBM_PEAK_GBS:.0f} GB/s | {p['torch_fill_gbps'] / HBM_PEAK_GBS:.3f} |", "",
+             f"Device: {p['device']}, {p['compute_units']} compute units, "
+             f"{p['hbm_bytes'] / 2**30:.0f} GiB of device memory.", "", "rocminfo (first GPU agent):", ""]
+    lines += [f"    {x}" for x in p["rocminfo"]]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -714,7 +831,14 @@ def main():
                     help="print the markdown summary of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--summarize-util", metavar="UTIL_DIR",
                     help="print the markdown summary of a rocprofv3 --pmc run of UTIL_COUNTERS and exit")
+    ap.add_argument("--peaks", action="store_true",
+                    help="print device facts and measured copy / fill / bf16 MFMA peaks (markdown) and exit")
     args = ap.parse_args()
+    if args.peaks:
+        import torch
+        assert torch.cuda.is_available(), "--peaks needs a GPU"
+        sys.stdout.write(summarize_peaks(measure_peaks(), "python3 bench.py --peaks"))
+        return
     if args.summarize_trace:
         cmd = ["rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run -- "
                "python3 $R/bench.py --steps 20 --warmup 2 --no-cpu --only-core > $OUT/kt_bench.json",

@@ -14,6 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
+# peak probes for the benchmark's roofline denominators (not part of libkda)
+PROBE_SRC = "kda_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libkda_probe.so")
 SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_copy.hip", "kda_ckpt_int8.hip", "kda_conv.hip",
            "kda_index.cpp", "kda_noalloc.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
@@ -35,18 +38,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -39,6 +39,21 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(K.EXPORTS)
 
 
+def test_probe_library_exports_and_rejects():
+    """libkda_probe.so (the benchmark's peak probes, not part of the API) loads,
+    exports its three probes, and rejects bad sizes before any launch."""
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(K.LIB_PATH), "libkda_probe.so"))
+    for n in ("kda_probe_mfma_bf16", "kda_probe_copy", "kda_probe_fill"):
+        assert hasattr(lib, n), n
+    lib.kda_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.kda_probe_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+    lib.kda_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.kda_probe_copy(FAKE, FAKE, 4096 + 16, None) != 0      # not whole 4 KiB pieces
+    assert lib.kda_probe_copy(FAKE + 8, FAKE, 4096, None) != 0       # misaligned
+    assert lib.kda_probe_fill(FAKE, 0, 0, None) != 0
+    assert lib.kda_probe_mfma_bf16(FAKE, 0, 10, None) != 0
+
+
 def pool(**kw):
     d = dict(base=FAKE, page_bytes=MiB2, num_pages=16, num_heads=32, d_k=128)
     d.update(kw)
