@@ -47,6 +47,10 @@ kda_status ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Largest accepted start position: positions plus a sequence length (at most
+// 2^30) and a hash block stay far from int64 overflow.
+constexpr int64_t kMaxStartPos = (int64_t)1 << 62;
+
 // ---- optional per-kernel timing ------------------------------------------
 struct TimedLaunch {
   const char* name;
@@ -220,8 +224,8 @@ kda_status kda::prefill_impl(const kda_pool* pool, const void* q, const void* k,
     if (len < 0) return fail(KDA_ERR_SEQ, "cu_seqlens decreases at %d", i);
     if (len > (int64_t)1 << 30) return fail(KDA_ERR_SEQ, "sequence %d longer than 2^30", i);
     const int64_t sp = start_pos ? start_pos[i] : 0;
-    if (sp < 0 || sp % 64 != 0)
-      return fail(KDA_ERR_SEQ, "start_pos[%d] = %lld must be a non-negative multiple of 64", i,
+    if (sp < 0 || sp % 64 != 0 || sp > kMaxStartPos)
+      return fail(KDA_ERR_SEQ, "start_pos[%d] = %lld must be a multiple of 64 in [0, 2^62]", i,
                   (long long)sp);
     total_chunks += (len + 63) / 64;
   }
@@ -554,7 +558,7 @@ kda_status kda_short_conv(const kda_conv_pool* cpool, const void* x, const float
     if (len < 0) return fail(KDA_ERR_SEQ, "%s: cu_seqlens decreases at %d", what, i);
     if (len > (int64_t)1 << 30) return fail(KDA_ERR_SEQ, "%s: sequence %d longer than 2^30", what, i);
     const int64_t sp = start_pos ? start_pos[i] : 0;
-    if (sp < 0) return fail(KDA_ERR_SEQ, "%s: start_pos[%d] < 0", what, i);
+    if (sp < 0 || sp > kMaxStartPos) return fail(KDA_ERR_SEQ, "%s: start_pos[%d] outside [0, 2^62]", what, i);
     const int32_t po = state_out_page ? state_out_page[i] : -1;
     total_chunks += len > 0 ? (len + 63) / 64 : (po >= 0 ? 1 : 0);
   }

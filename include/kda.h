@@ -154,7 +154,7 @@ size_t kda_prefill_workspace_min_bytes(const kda_pool* pool, int32_t num_seqs, i
  *   cu_seqlens     [num_seqs+1]  int64, cu_seqlens[0] == 0, non-decreasing;
  *                  sequence s owns rows [cu_seqlens[s], cu_seqlens[s+1]).
  *   start_pos      [num_seqs]    int64 or NULL (all 0): absolute position of the
- *                  sequence's first token; must be a multiple of chunk_size.  A
+ *                  sequence's first token; a multiple of chunk_size in [0, 2^62].  A
  *                  resume at boundary B passes start_pos = B and the restored
  *                  page as state_in_page.
  *   state_in_page  [num_seqs]    int32 or NULL: page holding S before the first
@@ -356,7 +356,7 @@ int64_t kda_conv_workspace_bytes(int32_t num_seqs, int32_t num_ckpts);
  * x : [T, C] (cpool->dtype, device), w : [C][W] fp32 (device), y : [T, C]
  * (out_dtype, device; may not alias x).  Sequences as in kda_prefill_chunked:
  * cu_seqlens [num_seqs+1] int64 host; start_pos [num_seqs] host or NULL (any
- * non-negative value); state_in_page / state_out_page [num_seqs] int32 host or
+ * value in [0, 2^62]); state_in_page / state_out_page [num_seqs] int32 host or
  * NULL (-1 = zero window / not written); checkpoints (ckpt_cu, ckpt_pos,
  * ckpt_page, host) at multiples of hash_block inside (start, start+len] receive
  * the window of the hash_block-aligned position, written in the same pass.  An

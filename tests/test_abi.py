@@ -140,6 +140,7 @@ def _prefill_status(p=None, T=1024, **kw):
     (dict(cu_seqlens=[0, 512, 256]), K.KDA_ERR_SEQ),
     (dict(start_pos=[100]), K.KDA_ERR_SEQ),
     (dict(start_pos=[-64]), K.KDA_ERR_SEQ),
+    (dict(start_pos=[(1 << 62) + 64]), K.KDA_ERR_SEQ),   # past the largest accepted position
     (dict(q=0), K.KDA_ERR_NULL),
     (dict(o=0), K.KDA_ERR_NULL),
     (dict(q=FAKE + 8), K.KDA_ERR_SHAPE),
@@ -395,6 +396,7 @@ def test_conv_pool_validation(pkw, status):
     (dict(cu_seqlens=[2, 10]), K.KDA_ERR_SEQ),
     (dict(cu_seqlens=[0, 10, 5]), K.KDA_ERR_SEQ),
     (dict(start_pos=[-1]), K.KDA_ERR_SEQ),
+    (dict(start_pos=[(1 << 62) + 1]), K.KDA_ERR_SEQ),
     (dict(state_in_page=[16]), K.KDA_ERR_PAGE_RANGE),
     (dict(state_out_page=[-3]), K.KDA_ERR_PAGE_RANGE),
     (dict(state_in_page=[2], state_out_page=[2]), K.KDA_ERR_PAGE_ALIAS),
