@@ -251,12 +251,13 @@ def test_conv_decode_shape(dtype):
 
 
 @pytest.mark.parametrize("dtype,W", [("bf16", 4), ("f32", 3), ("bf16", 2)])
-def test_conv_update_matches_short_conv(dtype, W):
+def test_conv_update_matches_short_conv(dtype, W, monkeypatch):
     """kda_short_conv_update (device page tables, one token per request) gives
     the bits of kda_short_conv on the same 1-token sequences: y and the new
     windows; in place (page_out == page_in) as well; a request with a page
     index outside the pool gets NaN outputs and touches no page; outputs match
     the oracle within the rounding bound."""
+    monkeypatch.delenv("KDA_VALIDATE", raising=False)  # the device-side handling is under test
     C, n = 3 * 32 * 128 // (1 if dtype == "bf16" else 2), 200
     x = G.conv_inputs(91 + W, n, C, dtype)
     w = G.conv_weights(91 + W, C, W)
@@ -328,3 +329,56 @@ def test_conv_full_size_8k():
     assert np.array_equal(got, to_bits(finals[0], dtype))
     for i, v in enumerate(ck[0]):
         assert np.array_equal(cp.window_bits(1 + i)[0], to_bits(v, dtype)), f"checkpoint {P[i]}"
+
+
+def test_conv_update_validate_mode(monkeypatch):
+    """With KDA_VALIDATE=1 kda_short_conv_update reads the page tables back and
+    checks them on the host first: a valid call gives the bits of the unchecked
+    one; an index outside the pool, a repeated output page and an input page
+    that is another request's output are rejected with the documented status,
+    and no page or output changes."""
+    dtype, W, C, n = "bf16", 4, 2048, 8
+    x = G.conv_inputs(17, n, C, dtype)
+    w = G.conv_weights(17, C, W)
+    wins = G.conv_inputs(18, n * (W - 1), C, dtype)
+    xd, wd = dev(x, dtype), torch.from_numpy(w).cuda()
+
+    def fresh():
+        cp = ConvPool(2 * n, C, W, dtype)
+        for r in range(n):
+            cp.set_window(r, to64(wins[r * (W - 1):(r + 1) * (W - 1)], dtype))
+        return cp
+
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    pout = torch.arange(n, 2 * n, dtype=torch.int32, device="cuda")
+    runs = []
+    for val in (None, "1"):
+        if val is None:
+            monkeypatch.delenv("KDA_VALIDATE", raising=False)
+        else:
+            monkeypatch.setenv("KDA_VALIDATE", val)
+        cp = fresh()
+        y = torch.empty((n, C), dtype=torch.bfloat16, device="cuda")
+        K.kda_short_conv_update(cp.pool, xd, wd, y, pin, pout)
+        torch.cuda.synchronize()
+        runs.append((y.view(torch.int16).cpu(), cp.buf.cpu()))
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+    def with_(t, i, val):
+        t = t.clone()
+        t[i] = val
+        return t
+
+    for bad_in, bad_out, status in [
+            (with_(pin, 2, 2 * n + 3), pout, K.KDA_ERR_PAGE_RANGE),
+            (pin, with_(pout, 5, -1), K.KDA_ERR_PAGE_RANGE),
+            (pin, with_(pout, 7, n), K.KDA_ERR_PAGE_ALIAS),       # output page n twice
+            (with_(pin, 1, n), pout, K.KDA_ERR_PAGE_ALIAS)]:      # request 0's output read by request 1
+        cp = fresh()
+        before = cp.buf.clone()
+        y = torch.full((n, C), 3.0, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(K.KdaError) as e:
+            K.kda_short_conv_update(cp.pool, xd, wd, y, bad_in, bad_out)
+        assert e.value.status == status, (e.value, status)
+        torch.cuda.synchronize()
+        assert torch.equal(cp.buf, before) and bool(torch.all(y == 3.0))

@@ -123,9 +123,10 @@ def test_decode_256_full():
     assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"], (e_o, e_s)
 
 
-def test_decode_bad_page_is_loud_and_harmless():
+def test_decode_bad_page_is_loud_and_harmless(monkeypatch):
     """A page index outside the pool touches no state and yields NaN outputs for
     that request only (the kernel checks every index before using it)."""
+    monkeypatch.delenv("KDA_VALIDATE", raising=False)  # the device-side handling is under test
     n, H, D = 3, 2, 64
     pb = PoolBuf(4, H, D)
     s0 = G.random_states(3, n, H, D)
@@ -233,7 +234,8 @@ def test_verify_oracle(dtype, D, ntok):
     assert worst <= TOL[dtype], worst
 
 
-def test_verify_bad_page_is_loud_and_harmless():
+def test_verify_bad_page_is_loud_and_harmless(monkeypatch):
+    monkeypatch.delenv("KDA_VALIDATE", raising=False)  # the device-side handling is under test
     n, H, D, ntok = 3, 2, 64, 3
     s0, d = _verify_setup(n, H, D, ntok, "bf16", 7)
     di = {k: dev(v, "bf16") for k, v in d.items()}
@@ -254,3 +256,70 @@ def test_verify_bad_page_is_loud_and_harmless():
     w = pb.page_bytes // 4
     for p in range(n + ntok, n + 2 * ntok - 1):  # request 1's valid output pages stay untouched
         assert np.array_equal(before[p * w:(p + 1) * w], after[p * w:(p + 1) * w])
+
+
+def test_validate_mode_checks_page_tables(monkeypatch):
+    """With KDA_VALIDATE=1 the decode page tables are read back and checked on
+    the host before anything runs: a valid call gives the bits of the unchecked
+    one (single token and verify form); an index outside the pool, a repeated
+    output page and an input page that is another request's output are rejected
+    with the documented status, and the pool and the outputs stay untouched."""
+    n, H, D, ntok = 4, 2, 64, 2
+    s0 = G.random_states(5, n, H, D)
+    d = G.kda_tokens(5, H, D, 0, n * ntok, "bf16")
+    di = {k: dev(v, "bf16") for k, v in d.items()}
+
+    def fresh():
+        pb = PoolBuf(n + n * ntok, H, D)
+        for r in range(n):
+            pb.set_states(r, s0[r])
+        return pb
+
+    def step(pb, o, pin, pout, tokens):
+        if tokens == 1:
+            K.kda_decode_step(pb.pool, di["q"][:n], di["k"][:n], di["v"][:n], di["g"][:n],
+                              di["beta"][:n], o, pin, pout)
+        else:
+            K.kda_decode_verify(pb.pool, di["q"], di["k"], di["v"], di["g"], di["beta"], o, tokens,
+                                pin, pout)
+
+    pin = torch.arange(n, dtype=torch.int32, device="cuda")
+    for tokens in (1, ntok):
+        pout = torch.arange(n, n + n * tokens, dtype=torch.int32, device="cuda")
+        runs = []
+        for val in (None, "1"):
+            if val is None:
+                monkeypatch.delenv("KDA_VALIDATE", raising=False)
+            else:
+                monkeypatch.setenv("KDA_VALIDATE", val)
+            pb = fresh()
+            o = torch.empty((n * tokens, H, D), dtype=torch.bfloat16, device="cuda")
+            step(pb, o, pin, pout, tokens)
+            torch.cuda.synchronize()
+            runs.append((o.view(torch.int16).cpu(), pb.buf.cpu()))
+        assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1]), tokens
+
+    def with_(t, i, val):
+        t = t.clone()
+        t[i] = val
+        return t
+
+    p1 = torch.arange(n, 2 * n, dtype=torch.int32, device="cuda")
+    p2 = torch.arange(n, n + n * ntok, dtype=torch.int32, device="cuda")
+    cases = [
+        (1, with_(pin, 2, 100), p1, K.KDA_ERR_PAGE_RANGE),
+        (1, pin, with_(p1, 1, -1), K.KDA_ERR_PAGE_RANGE),
+        (1, pin, with_(p1, 3, n), K.KDA_ERR_PAGE_ALIAS),         # output page n twice
+        (1, with_(pin, 1, n), p1, K.KDA_ERR_PAGE_ALIAS),         # request 0's output read by request 1
+        (ntok, pin, with_(p2, 1, n), K.KDA_ERR_PAGE_ALIAS),      # request 0's two tokens share a page
+        (ntok, pin, with_(p2, 7, n + n * ntok), K.KDA_ERR_PAGE_RANGE),
+    ]
+    for tokens, bad_in, bad_out, status in cases:
+        pb = fresh()
+        before = pb.buf.clone()
+        o = torch.full((n * tokens, H, D), 3.0, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(K.KdaError) as e:
+            step(pb, o, bad_in, bad_out, tokens)
+        assert e.value.status == status, (tokens, e.value, status)
+        torch.cuda.synchronize()
+        assert torch.equal(pb.buf, before) and bool(torch.all(o == 3.0))
