@@ -206,7 +206,8 @@ def test_verify_equals_sequential_steps_bitwise():
             assert np.array_equal(pb.states(n + r * ntok + t), pb.states(base + n + r * ntok + t)), (r, t)
 
 
-@pytest.mark.parametrize("dtype,D,ntok", [("bf16", 128, 6), ("f32", 64, 5)])
+@pytest.mark.parametrize("dtype,D,ntok", [("bf16", 128, 6), ("f32", 64, 5),
+                                          ("f32", 128, 64), ("bf16", 64, 64)])  # 64: the most per call
 def test_verify_oracle(dtype, D, ntok):
     """Each request's ntok tokens against the oracle run over them with a
     checkpoint after every token."""
