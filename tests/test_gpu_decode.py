@@ -324,3 +324,60 @@ def test_validate_mode_checks_page_tables(monkeypatch):
         assert e.value.status == status, (tokens, e.value, status)
         torch.cuda.synchronize()
         assert torch.equal(pb.buf, before) and bool(torch.all(o == 3.0))
+
+
+def test_serving_loop_graph_replay_bitwise():
+    """A serving loop captured once in a HIP graph: 8 single-token decode steps
+    in place through a device page table, a 3-token verify into fresh pages,
+    then a checkpoint copy of each request's first verified state.  Replayed
+    three times from the same starting pool, with eager work and
+    synchronisation between replays: every replay leaves the outputs and the
+    pool bit-identical to the eager run."""
+    n, H, D, steps, ntok = 16, 4, 128, 8, 3
+    s0 = G.random_states(21, n, H, D)
+    d = G.kda_tokens(21, H, D, 0, (steps + ntok) * n, "bf16")
+    di = {k: dev(v, "bf16") for k, v in d.items()}
+    pb = PoolBuf(n + n * ntok + n, H, D)
+    for r in range(n):
+        pb.set_states(r, s0[r])
+    start = pb.buf.clone()
+    pt = torch.arange(n, dtype=torch.int32, device="cuda")
+    pv = torch.arange(n, n + n * ntok, dtype=torch.int32, device="cuda")
+    src = [n + r * ntok for r in range(n)]
+    dst = [n + n * ntok + r for r in range(n)]
+    o = torch.empty((steps, n, H, D), dtype=torch.bfloat16, device="cuda")
+    ov = torch.empty((n * ntok, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def loop():
+        for t in range(steps):
+            sl = slice(t * n, (t + 1) * n)
+            K.kda_decode_step(pb.pool, di["q"][sl], di["k"][sl], di["v"][sl], di["g"][sl],
+                              di["beta"][sl], o[t], pt, pt)
+        b = steps * n
+        K.kda_decode_verify(pb.pool, di["q"][b:], di["k"][b:], di["v"][b:], di["g"][b:],
+                            di["beta"][b:], ov, ntok, pt, pv)
+        K.kda_checkpoint_write(pb.pool, src, dst)
+
+    loop()
+    torch.cuda.synchronize()
+    ref = (o.view(torch.int16).cpu(), ov.view(torch.int16).cpu(), pb.buf.cpu())
+    pb.buf.copy_(start)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop()  # warm-up on a side stream before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    for _ in range(3):
+        pb.buf.copy_(start)
+        o.fill_(float("nan"))
+        ov.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16).cpu(), ref[0])
+        assert torch.equal(ov.view(torch.int16).cpu(), ref[1])
+        assert torch.equal(pb.buf.cpu(), ref[2])
