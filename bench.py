@@ -225,19 +225,28 @@ def to_dev(x, dtype):
 
 def timed(fn, steps, warmup):
     """Run fn warmup times, then time exactly `steps` calls between two device
-    synchronisations (HIP events on the current stream + host clock)."""
+    synchronisations (HIP events on the current stream + host clock).  Python's
+    cyclic garbage collector is paused over the timed calls, as timeit does: a
+    full collection in this process takes ~35 ms of host time, which would
+    stall the enqueueing of kernels."""
+    import gc
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    gc.collect()
+    gc.disable()
+    try:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        gc.enable()
     return e0.elapsed_time(e1) / 1e3, wall
 
 
@@ -256,11 +265,16 @@ def kernel_times(K, fn, reps):
     return {name: {"launches": n, "avg_ms": ms / max(n, 1)} for name, (n, ms) in stats.items()}
 
 
-def bench_prefill(K, G, steps, warmup):
-    import torch
+def prefill_inputs(G):
+    """The 8K workload's inputs on the host and on the device."""
     w = G.PREFILL_8K
     d = G.kda_tokens(w.seed, w.H, w.D, 0, w.T, w.dtype)
-    di = {k: to_dev(v, w.dtype) for k, v in d.items()}
+    return w, d, {k: to_dev(v, w.dtype) for k, v in d.items()}
+
+
+def bench_prefill(K, G, steps, warmup, inputs=None):
+    import torch
+    w, d, di = inputs or prefill_inputs(G)
     num_pages = 8
     pool_buf = torch.zeros(num_pages * w.page_bytes // 4, dtype=torch.int32, device="cuda")
     pool = K.make_pool(pool_buf, w.page_bytes, num_pages, w.H, w.D)
@@ -868,8 +882,34 @@ def main():
     import kda_inputs as G
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    # The GPU legs run first and the prefill right after them, with its
+    # inputs already on the device, so that it is not timed on a GPU that is
+    # just leaving its idle state (on one box, timed first, its first ~80
+    # calls drifted from 261 to 277 and back to 255 us; after the decode leg
+    # they ran at 252-254 us from the first call).  Its own W warm-up and K
+    # timed calls are unchanged.
     log("prefill: generating inputs")
-    w, d, dev_s, wall_s, kt, graph = bench_prefill(K, G, args.steps, args.warmup)
+    pre_in = prefill_inputs(G)
+    legs = {}
+    if not args.only_prefill:
+        log("decode: 256 requests x 32 heads")
+        legs["decode"] = bench_decode(K, G)
+        torch.cuda.empty_cache()
+        log(f"decode: {legs['decode']}")
+        legs["checkpoint_copy"] = bench_copy(K, steps=20, warmup=3)
+        log(f"copy: {legs['checkpoint_copy']}")
+        legs["checkpoint_int8"] = bench_int8(K)
+        log(f"int8: {legs['checkpoint_int8']}")
+        legs["verify"] = bench_verify(K, G)
+        log(f"verify: {legs['verify']}")
+        legs["short_conv"] = bench_conv(K, G)
+        log(f"conv: {legs['short_conv']}")
+        legs["short_conv_decode"] = bench_conv_decode(K, G)
+        log(f"conv decode: {legs['short_conv_decode']}")
+        torch.cuda.empty_cache()
+
+    w, d, dev_s, wall_s, kt, graph = bench_prefill(K, G, args.steps, args.warmup, pre_in)
+    del pre_in
     ms_step = 1e3 * dev_s / args.steps
     tok_s = w.T * args.steps / dev_s
     log(f"prefill: {ms_step:.3f} ms/step, {tok_s / 1e6:.2f} M tokens/s; kernels {kt}")
@@ -912,22 +952,9 @@ def main():
         "prefill_wall_s": wall_s,
         "prefill_graph": graph,
     }
+    out.update(legs)
     if not args.only_prefill:
-        log("decode: 256 requests x 32 heads")
-        out["decode"] = bench_decode(K, G)
-        torch.cuda.empty_cache()
-        log(f"decode: {out['decode']}")
-        out["checkpoint_copy"] = bench_copy(K, steps=20, warmup=3)
-        log(f"copy: {out['checkpoint_copy']}")
-        out["checkpoint_int8"] = bench_int8(K)
-        log(f"int8: {out['checkpoint_int8']}")
-        out["verify"] = bench_verify(K, G)
-        log(f"verify: {out['verify']}")
-        out["short_conv"] = bench_conv(K, G)
-        log(f"conv: {out['short_conv']}")
-        out["short_conv_decode"] = bench_conv_decode(K, G)
-        log(f"conv decode: {out['short_conv_decode']}")
-        out["prefix_index"] = bench_index(K, G)
+        out["prefix_index"] = bench_index(K, G)  # host CPU work, after the GPU legs
         log(f"index: {out['prefix_index']}")
     if not args.only_prefill and not args.only_core:
         log("varlen resume: 16 sequences")
