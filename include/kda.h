@@ -150,6 +150,8 @@ size_t kda_prefill_workspace_min_bytes(const kda_pool* pool, int32_t num_seqs, i
  *   v       : [total_tokens, H, d_v]
  *   beta    : [total_tokens, H]
  *   o       : [total_tokens, H, d_v] written in `out_dtype`
+ *   q, k, v, g and o 16-byte aligned (KDA_ERR_SHAPE otherwise); o must not
+ *   overlap an input.
  * Host metadata (read before return):
  *   cu_seqlens     [num_seqs+1]  int64, cu_seqlens[0] == 0, non-decreasing;
  *                  sequence s owns rows [cu_seqlens[s], cu_seqlens[s+1]).
