@@ -507,21 +507,36 @@ def bench_verify(K, G, steps=20, warmup=5, n=128, ntok=4):
 
 def bench_int8(K, steps=20, warmup=10):
     """int8 compressed checkpoints: quantise 256 active pages (32 heads, d=128)
-    into a compressed pool, and dequantise them back into fp32 pages."""
+    into a compressed pool, and dequantise them back into fp32 pages.  Calls
+    cycle through three sets of source pages (1.5 GiB of fp32 pages, 415 MB of
+    compressed ones), so that no call reads what the previous call left in
+    the memory-side cache."""
     import torch
-    H, D, n = 32, 128, 256
+    H, D, n, R = 32, 128, 256, 3
     sb = H * D * D * 4
-    pool_buf = torch.randn(2 * n * sb // 4, device="cuda") / np.sqrt(D)
-    pool = K.make_pool(pool_buf, sb, 2 * n, H, D)
+    pool_buf = torch.randn((R + 1) * n * sb // 4, device="cuda") / np.sqrt(D)
+    pool = K.make_pool(pool_buf, sb, (R + 1) * n, H, D)
     hb = K.kda_ckpt_int8_head_bytes(D, D)
     qpb = (H * hb + 255) // 256 * 256
-    qbuf = torch.zeros(n * qpb, dtype=torch.uint8, device="cuda")  # touched before timing
-    qpool = K.make_pool(qbuf, qpb, n, H, D)
-    src, dst = list(range(n)), list(range(n, 2 * n))
-    out = {"pages": n, "page_bytes": sb, "compressed_page_bytes": H * hb}
-    for name, fn, kern in (
-            ("write", lambda: K.kda_checkpoint_write_int8(pool, src, qpool, src), "kda_ckpt_quant"),
-            ("restore", lambda: K.kda_checkpoint_restore_int8(qpool, src, pool, dst), "kda_ckpt_dequant")):
+    qbuf = torch.zeros(R * n * qpb, dtype=torch.uint8, device="cuda")  # touched before timing
+    qpool = K.make_pool(qbuf, qpb, R * n, H, D)
+    sets = [list(range(r * n, (r + 1) * n)) for r in range(R)]
+    dst = list(range(R * n, (R + 1) * n))
+    for r in range(R):  # every compressed set holds real checkpoints before the restores
+        K.kda_checkpoint_write_int8(pool, sets[r], qpool, sets[r])
+    it = [0]
+
+    def write():
+        r = it[0] % R
+        it[0] += 1
+        K.kda_checkpoint_write_int8(pool, sets[r], qpool, sets[r])
+
+    def restore():
+        r = it[0] % R
+        it[0] += 1
+        K.kda_checkpoint_restore_int8(qpool, sets[r], pool, dst)
+    out = {"pages": n, "page_bytes": sb, "compressed_page_bytes": H * hb, "source_sets": R}
+    for name, fn, kern in (("write", write, "kda_ckpt_quant"), ("restore", restore, "kda_ckpt_dequant")):
         dev_s, _ = timed(fn, steps, warmup)
         kt = kernel_times(K, fn, steps)
         moved = n * (sb + H * hb)  # fp32 page one way, compressed page the other
@@ -538,7 +553,9 @@ def bench_conv(K, G, steps=20, warmup=5, T=8192, C=3 * 32 * 128, W=4):
     call), with the window checkpointed at every 512-token boundary and a
     final window page."""
     import torch
-    x = to_dev(G.conv_inputs(11, T, C, "bf16"), "bf16")
+    # three distinct input batches (600 MB together, more than the memory-side
+    # cache holds), so that no call finds the previous call's input cached
+    xs = [to_dev(G.conv_inputs(11 + s, T, C, "bf16"), "bf16") for s in range(3)]
     wt = torch.from_numpy(G.conv_weights(11, C, W)).cuda()
     y = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
     P = list(range(512, T + 1, 512))
@@ -548,7 +565,11 @@ def bench_conv(K, G, steps=20, warmup=5, T=8192, C=3 * 32 * 128, W=4):
     cpool = K.make_conv_pool(cbuf, pb, len(P) + 1, C, W, K.KDA_BF16)
     wsb = torch.empty(K.kda_conv_workspace_bytes(1, len(P)), dtype=torch.uint8, device="cuda")
 
+    it = [0]
+
     def step():
+        x = xs[it[0] % len(xs)]
+        it[0] += 1
         K.kda_short_conv(cpool, x, wt, y, [0, T], state_out_page=[0], ckpt_cu=[0, len(P)],
                          ckpt_pos=P, ckpt_page=list(range(1, 1 + len(P))), workspace=wsb)
     dev_s, _ = timed(step, steps, warmup)
