@@ -22,7 +22,10 @@
 // directions are HBM streams; state accesses are non-temporal.  The write is
 // read-dominated (4 bytes in per byte out), so each quantising thread keeps
 // four rows' loads in flight (measured: 147 -> 121 us for 256 pages of
-// 32 heads; the restore, write-dominated, streams best with one vector).
+// 32 heads).  The restore reads a compressed page that is usually cold (not
+// in the memory-side cache): each restoring thread loads two rows' codes and
+// scales before its first store (256 pages of 32 heads, cold: one row 133 us,
+// two rows 106 us, four rows 114 us).
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -34,7 +37,9 @@ template <int D> struct QuantShape {
   static constexpr int WPH = D / RPW;     // restore workgroups per head
   static constexpr int QRPT = 4;          // rows per quantising thread
   static constexpr int QWPH = WPH / QRPT; // quantise workgroups per head
-  static_assert(QWPH >= 1, "rows per quantising thread");
+  static constexpr int RRPT = 2;          // rows per restoring thread
+  static constexpr int RWPH = WPH / RRPT; // restore workgroups per head
+  static_assert(QWPH >= 1 && RWPH >= 1, "rows per thread");
 };
 
 __device__ __forceinline__ uint32_t code_of(float x, float scale) {
@@ -122,22 +127,31 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void dequant_kernel(QuantArgs a) {
   using QS = QuantShape<D>;
-  const int per_pair = a.H * QS::WPH;
+  constexpr int RPT = QS::RRPT;
+  const int per_pair = a.H * QS::RWPH;
   const int pair = blockIdx.x / per_pair, rem = blockIdx.x % per_pair;
   if (pair >= a.npairs) return;
-  const int h = rem / QS::WPH, row = (rem % QS::WPH) * QS::RPW + threadIdx.x / QS::LPR;
+  const int h = rem / QS::RWPH, row0 = (rem % QS::RWPH) * QS::RPW * RPT + threadIdx.x / QS::LPR;
   const int c = (threadIdx.x % QS::LPR) * 4;
   const uint8_t* qh = a.qpool + a.src[pair] * a.qpage_bytes + (int64_t)h * int8_head_bytes(D);
-  const uint32_t packed = *reinterpret_cast<const uint32_t*>(qh + row * D + c);
-  const float scale = *reinterpret_cast<const float*>(qh + (int64_t)D * D + 4 * row);
-  f32x4 y;
-  y.x = (float)(int8_t)(packed & 0xffu) * scale;
-  y.y = (float)(int8_t)((packed >> 8) & 0xffu) * scale;
-  y.z = (float)(int8_t)((packed >> 16) & 0xffu) * scale;
-  y.w = (float)(int8_t)(packed >> 24) * scale;
-  float* dst = reinterpret_cast<float*>(a.pool + a.dst[pair] * a.page_bytes) + (int64_t)h * D * D +
-               row * D + c;
-  __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(dst));
+  uint32_t packed[RPT];
+  float scale[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    const int row = row0 + k * QS::RPW;
+    packed[k] = *reinterpret_cast<const uint32_t*>(qh + row * D + c);
+    scale[k] = *reinterpret_cast<const float*>(qh + (int64_t)D * D + 4 * row);
+  }
+  float* dst = reinterpret_cast<float*>(a.pool + a.dst[pair] * a.page_bytes) + (int64_t)h * D * D + c;
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    f32x4 y;
+    y.x = (float)(int8_t)(packed[k] & 0xffu) * scale[k];
+    y.y = (float)(int8_t)((packed[k] >> 8) & 0xffu) * scale[k];
+    y.z = (float)(int8_t)((packed[k] >> 16) & 0xffu) * scale[k];
+    y.w = (float)(int8_t)(packed[k] >> 24) * scale[k];
+    __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(dst + (row0 + k * QS::RPW) * D));
+  }
 }
 
 hipError_t launch_quant(int D, const QuantArgs& a, hipStream_t st) {
@@ -152,10 +166,10 @@ hipError_t launch_quant(int D, const QuantArgs& a, hipStream_t st) {
 
 hipError_t launch_dequant(int D, const QuantArgs& a, hipStream_t st) {
   if (D == 128)
-    hipLaunchKernelGGL(dequant_kernel<128>, dim3(a.npairs * a.H * QuantShape<128>::WPH), dim3(256),
+    hipLaunchKernelGGL(dequant_kernel<128>, dim3(a.npairs * a.H * QuantShape<128>::RWPH), dim3(256),
                        0, st, a);
   else
-    hipLaunchKernelGGL(dequant_kernel<64>, dim3(a.npairs * a.H * QuantShape<64>::WPH), dim3(256), 0,
+    hipLaunchKernelGGL(dequant_kernel<64>, dim3(a.npairs * a.H * QuantShape<64>::RWPH), dim3(256), 0,
                        st, a);
   return hipGetLastError();
 }
