@@ -156,15 +156,6 @@ __device__ __forceinline__ Frag<Op> frag_fm(const Op* x, int row_tile, int k_ste
   return f;
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (linear id i runs on
-// XCD i % 8).  xcd_contiguous(i, n) is a bijection on [0, n) that hands each
-// XCD one contiguous range of tiles (the first n % 8 XCDs one tile more), so
-// tiles that share data -- neighbours in the range -- share one L2.
-__device__ __forceinline__ int xcd_contiguous(int i, int n) {
-  const int q = n >> 3, r = n & 7, x = i & 7, k = i >> 3;
-  return x * q + min(x, r) + k;
-}
-
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Row/column of element r (0..3) of a 16x16 accumulator held by `lane`.
